@@ -1,0 +1,30 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests must never silently pass without a GPU: skip them loudly
+    # when no device is visible (the driver selects them with -m gpu on a
+    # GPU machine, where torch.cuda.is_available() is True).
+    try:
+        import torch
+        have_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        have_gpu = False
+    if have_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible in this process")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)
