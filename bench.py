@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed binary (XOR + popcount) hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+Prints ONE JSON line.  A step is one pass of the hot path over one batch of
+synthetic input, inputs already resident in HBM:
+
+  gemv_4096 (default): pack the bf16 activation row (1 x 4096) and run the
+      alpha-scaled fp32 binary GEMV against a packed 4096 x 4096 weight
+      matrix.  Step i reads weight copy i mod R from a ring of R = 256
+      distinct copies (512 MiB, twice the 256 MB Infinity Cache), so every
+      step streams its weights from HBM as a decoder walking many layers
+      would.  Steps are captured in a HIP graph and replayed.  value = HBM
+      GB/s of algorithmic bytes per step.
+  ffn_4096: pack X (4096 x 4096 bf16) and run the alpha-scaled GEMM against
+      packed W (11008 x 4096).  value = binary GOPS (2*M*N*K / s).
+  chain_65536: pack X (65536 x 512 fp32), two sign->repack layers
+      (512->256->128) and an alpha-scaled last layer (128->64).
+      value = binary GOPS over the three layers.
+
+"roofline" reports the dominant kernel of the step: its algorithmic bytes
+(or binary ops) per launch divided by its average duration, measured here
+with HIP events on the stream it runs on, against the MI355X peak that
+bounds it.  "cpu_baseline" times the CPU oracle on a bounded sample of the
+same workload on this host's cores.  "secondary" repeats the measurement
+for the large-M GEMM (ffn_4096) so that both regimes appear in one record.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "binary GOPS (2·M·N·K bit-MAC/s) + batch-1 GEMV HBM GB/s vs peak"
+
+HBM_PEAK_GBS = 8000.0
+# VALU XOR + popcount issue peak, in binary ops (2 per bit-MAC) per second:
+# 256 CU x 64 lanes/clk x 2.4 GHz = 3.93e13 32-bit lane-ops/s; one 64-bit
+# word pair (64 bit-MACs = 128 binary ops) costs 4 lane-ops
+# (2 v_xor_b32 + 2 v_bcnt_u32_b32).
+VALU_LANE_OPS = 256 * 64 * 2.4e9
+ALU_PEAK_BINARY_OPS = VALU_LANE_OPS / 4 * 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="gemv_4096",
+                    choices=["gemv_4096", "ffn_4096", "chain_65536"])
+    ap.add_argument("--ring", type=int, default=256, help="distinct weight copies (gemv)")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="gemv only: override N (weight rows) for the streaming-rate variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# GPU legs
+
+
+def timed(fn, n, stream):
+    """Run fn() n times between two HIP events on `stream`; ms per call."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def gemv_leg(args, steps, warmup):
+    import torch
+    import packed_xor_popcount_amd as bnn
+    import workloads
+    dev = torch.device("cuda:0")
+    d = workloads.make("gemv_4096")
+    K = d["K"]
+    kw = bnn.words(K)
+    wp = bnn.pack_signs(d["w"].to(dev))
+    alpha = d["alpha"].to(dev)
+    N = wp.shape[0]
+    if args.rows:  # streaming-rate variant: tile the same rows up to args.rows
+        reps = -(-args.rows // N)
+        wp = wp.repeat(reps, 1)[: args.rows].contiguous()
+        alpha = alpha.repeat(reps)[: args.rows].contiguous()
+        N = args.rows
+    R = max(1, args.ring if not args.rows else max(1, min(args.ring, (1 << 30) // (N * kw * 8))))
+    wring = wp.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    del wp
+    g = workloads.generator(2002)
+    xring = workloads.normal(g, R, 1, K).to(torch.bfloat16).to(dev)
+    xring[0].copy_(d["x"].to(dev))
+    xp = torch.empty((1, kw), dtype=torch.int64, device=dev)
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(j):
+        bnn.pack_signs(xring[j], out=xp)
+        bnn.gemm_ex(xp, wring[j], K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
+
+    def gemv_only(j):
+        bnn.gemm_ex(xp, wring[j], K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
+
+    # eager warmup, then capture R steps (one per ring entry) in a HIP graph
+    for i in range(max(warmup, 1)):
+        step(i % R)
+    torch.cuda.synchronize()
+    graphs = {}
+
+    def graph_of(n, body):
+        key = (n, body.__name__)
+        if key not in graphs:
+            gr = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream(dev)
+            s.wait_stream(stream)
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(gr, stream=s):
+                    for j in range(n):
+                        body(j % R)
+            torch.cuda.synchronize()
+            graphs[key] = gr
+        return graphs[key]
+
+    full, rem = divmod(steps, R)
+    g_full = graph_of(R, step) if full else None
+    g_rem = graph_of(rem, step) if rem else None
+    for gr in (g_full, g_rem):
+        if gr is not None:
+            gr.replay()
+    torch.cuda.synchronize()
+
+    def run_steps():
+        for _ in range(full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    ms_total = timed(run_steps, 1, stream)
+    ms_step = ms_total / steps
+    # dominant kernel alone: R back-to-back GEMV launches in a graph
+    g_gemv = graph_of(R, gemv_only)
+    g_gemv.replay()
+    reps = max(1, steps // R)
+    ms_gemv = timed(g_gemv.replay, reps, stream) / R
+    bytes_gemv = N * kw * 8 + kw * 8 + N * 4 + N * 4          # Wp + xp + alpha + y
+    bytes_step = bytes_gemv + K * 2 + kw * 8                  # + x bf16 read + xp write
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    gops = 2.0 * N * K / (ms_step * 1e-3) / 1e9
+    achieved = bytes_gemv / (ms_gemv * 1e-3) / 1e9
+    return dict(
+        value=gbs, unit="GB/s", ms_per_step=ms_step, binary_gops=gops,
+        config={"workload": "gemv_4096" if not args.rows else f"gemv_4096_rows{N}", "M": 1,
+                "K": K, "N": N, "x_dtype": "bf16", "w_dtype": "fp32 (packed offline)",
+                "epilogue": "alpha-scaled fp32", "weight_ring": R,
+                "bytes_per_step": bytes_step, "hip_graph": True},
+        roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                  "kernel": "gemv_kernel (alpha-scaled)", "kernel_avg_us": ms_gemv * 1e3,
+                  "algorithmic_bytes_per_launch": bytes_gemv},
+        step_inputs=(d, N, K),
+    )
+
+
+def ffn_leg(steps, warmup):
+    import torch
+    import packed_xor_popcount_amd as bnn
+    import workloads
+    dev = torch.device("cuda:0")
+    d = workloads.make("ffn_4096")
+    K = d["K"]
+    x = d["x"].to(dev)
+    wp = bnn.pack_signs(d["w"].to(dev))
+    alpha = d["alpha"].to(dev)
+    M, N = x.shape[0], wp.shape[0]
+    xp = torch.empty((M, bnn.words(K)), dtype=torch.int64, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        bnn.pack_signs(x, out=xp)
+        bnn.gemm_ex(xp, wp, K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
+
+    def gemm_only():
+        bnn.gemm_ex(xp, wp, K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
+
+    for _ in range(max(warmup, 1)):
+        step()
+    ms_step = timed(step, steps, stream)
+    ms_gemm = timed(gemm_only, steps, stream)
+    ops = 2.0 * M * N * K
+    return dict(
+        value=ops / (ms_step * 1e-3) / 1e9, unit="binary GOPS", ms_per_step=ms_step,
+        config={"workload": "ffn_4096", "M": M, "K": K, "N": N, "x_dtype": "bf16",
+                "w_dtype": "fp32 (packed offline)", "epilogue": "alpha-scaled fp32"},
+        roofline={"bound": "alu", "achieved": ops / (ms_gemm * 1e-3) / 1e12,
+                  "peak": ALU_PEAK_BINARY_OPS / 1e12, "unit": "T binary-ops/s",
+                  "frac": ops / (ms_gemm * 1e-3) / ALU_PEAK_BINARY_OPS, "traffic": None,
+                  "kernel": "gemm_tiled_kernel (alpha-scaled)", "kernel_avg_us": ms_gemm * 1e3,
+                  "algorithmic_ops_per_launch": ops},
+        step_inputs=(d, N, K),
+    )
+
+
+def chain_leg(steps, warmup):
+    import torch
+    import packed_xor_popcount_amd as bnn
+    import workloads
+    dev = torch.device("cuda:0")
+    d = workloads.make("chain_65536")
+    dims = d["dims"]
+    x = d["x"].to(dev)
+    M = x.shape[0]
+    wps = [bnn.pack_signs(w.to(dev)) for w in d["weights"]]
+    alpha = d["alpha"].to(dev)
+    h0 = torch.empty((M, bnn.words(dims[0])), dtype=torch.int64, device=dev)
+    h1 = torch.empty((M, bnn.words(dims[1])), dtype=torch.int64, device=dev)
+    h2 = torch.empty((M, bnn.words(dims[2])), dtype=torch.int64, device=dev)
+    y = torch.empty((M, dims[3]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        bnn.pack_signs(x, out=h0)
+        bnn.gemm_sign_repack(h0, wps[0], dims[0], out=h1)
+        bnn.gemm_sign_repack(h1, wps[1], dims[1], out=h2)
+        bnn.gemm_u64_scaled(h2, wps[2], alpha, dims[2], out=y)
+
+    def layer1():
+        bnn.gemm_sign_repack(h0, wps[0], dims[0], out=h1)
+
+    for _ in range(max(warmup, 1)):
+        step()
+    ms_step = timed(step, steps, stream)
+    ms_l1 = timed(layer1, steps, stream)
+    ops = sum(2.0 * M * dims[i] * dims[i + 1] for i in range(3))
+    ops1 = 2.0 * M * dims[0] * dims[1]
+    return dict(
+        value=ops / (ms_step * 1e-3) / 1e9, unit="binary GOPS", ms_per_step=ms_step,
+        config={"workload": "chain_65536", "M": M, "dims": list(dims), "x_dtype": "fp32",
+                "hidden": "sign->repack u64", "epilogue": "alpha-scaled fp32"},
+        roofline={"bound": "alu", "achieved": ops1 / (ms_l1 * 1e-3) / 1e12,
+                  "peak": ALU_PEAK_BINARY_OPS / 1e12, "unit": "T binary-ops/s",
+                  "frac": ops1 / (ms_l1 * 1e-3) / ALU_PEAK_BINARY_OPS, "traffic": None,
+                  "kernel": "gemm_tiled_kernel (sign->repack, layer 1)",
+                  "kernel_avg_us": ms_l1 * 1e3, "algorithmic_ops_per_launch": ops1},
+        step_inputs=(d, None, None),
+    )
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the workload
+
+
+def cpu_baseline(workload, step_inputs, seconds):
+    import numpy as np
+    import oracle
+    import workloads
+    d, N, K = step_inputs
+    if workload == "gemv_4096":
+        wp = oracle.pack(d["w"].numpy())   # weights are packed offline, as on the GPU
+        alpha = d["alpha"].numpy()
+        xb = workloads.bf16_bits(d["x"])
+        kw = oracle.words(K)
+        bytes_step = N * kw * 8 + kw * 8 + N * 8 + K * 2 + kw * 8
+        n, t0 = 0, time.perf_counter()
+        while True:
+            xp = oracle.pack(xb)
+            oracle.gemm_scaled(xp, wp, alpha, K)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / n
+        return {"value": bytes_step / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} full gemv_4096 steps (pack x + scaled GEMV), {dt * 1e3:.1f} ms/step;"
+                          " the oracle splits rows over threads, and M=1 gives one thread"}
+    if workload == "ffn_4096":
+        rows = 8
+        xb = workloads.bf16_bits(d["x"][:rows])
+        wp = oracle.pack(d["w"].numpy())
+        alpha = d["alpha"].numpy()
+        cores = os.cpu_count() or 1
+        n, t0 = 0, time.perf_counter()
+        while True:
+            xp = oracle.pack(xb)
+            oracle.gemm_scaled(xp, wp, alpha, K, nthreads=cores)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = (time.perf_counter() - t0) / n
+        return {"value": 2.0 * rows * N * K / dt / 1e9, "unit": "binary GOPS",
+                "cores": min(cores, rows), "kind": "oracle",
+                "sample": f"{n} x {rows} rows of ffn_4096 (all 11008 columns), {dt:.2f} s each"}
+    # chain
+    rows = 2048
+    x = d["x"].numpy()[:rows]
+    ws = [w.numpy() for w in d["weights"]]
+    cores = os.cpu_count() or 1
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.chain(x, ws, d["alpha"].numpy(), nthreads=cores)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    dims = d["dims"]
+    ops = sum(2.0 * rows * dims[i] * dims[i + 1] for i in range(3))
+    return {"value": ops / dt / 1e9, "unit": "binary GOPS", "cores": cores, "kind": "oracle",
+            "sample": f"{n} x {rows}-row chain passes, {dt:.2f} s each"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this implementation has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a visible MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import packed_xor_popcount_amd as bnn
+    bnn.library()  # fail loudly if the HIP library is missing
+
+    defaults = {"gemv_4096": (1024, 64), "ffn_4096": (20, 3), "chain_65536": (50, 5)}
+    steps = args.steps if args.steps is not None else defaults[args.workload][0]
+    warmup = args.warmup if args.warmup is not None else defaults[args.workload][1]
+    log(f"[bench] workload={args.workload} steps={steps} warmup={warmup}")
+    if args.workload == "gemv_4096":
+        res = gemv_leg(args, steps, warmup)
+    elif args.workload == "ffn_4096":
+        res = ffn_leg(steps, warmup)
+    else:
+        res = chain_leg(steps, warmup)
+    log(f"[bench] {args.workload}: {res['value']:.1f} {res['unit']}, "
+        f"{res['ms_per_step'] * 1e3:.2f} us/step")
+
+    out = {
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u64",
+        "data": "synthetic (seeded, see workloads.py)", "config": res["config"],
+        "roofline": res["roofline"],
+    }
+    if "binary_gops" in res:
+        out["binary_gops"] = res["binary_gops"]
+    if args.workload == "gemv_4096" and not args.no_secondary and not args.rows:
+        sec = ffn_leg(10, 2)
+        log(f"[bench] secondary ffn_4096: {sec['value']:.1f} binary GOPS")
+        out["secondary"] = {"workload": "ffn_4096", "value": sec["value"], "unit": sec["unit"],
+                            "ms_per_step": sec["ms_per_step"], "roofline": sec["roofline"]}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(args.workload, res["step_inputs"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * bnn.h -- C-ABI of libbnn.so: packed binary (+1/-1) matrix products on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources cited by page title and section):
+ *
+ *   "Binary Math Effectiveness -- why / how / when", section 1 "The core
+ *   identity":
+ *     - encoding: a +1 is stored as bit 0 and a -1 as bit 1;
+ *     - for x, w in {+1,-1}^n with d = popcount(x_bits XOR w_bits),
+ *       <x, w> = n - 2d  (the library uses this XOR form);
+ *     - edge cases: pad bits encode +1 and the identity uses the logical
+ *       n, not 64 * words; n = 0 gives 0; a channel scale alpha = 0 gives a
+ *       scaled output of 0; real inputs are projected to -1 when <= 0 and
+ *       to +1 when > 0 before the identity is applied.
+ *   Same page, section 2.1 "Arithmetic": a length-K row takes ceil(K/64)
+ *   64-bit words, one XOR + popcount per word.
+ *   Same page, sections 2.2-2.3: a batch-1 product is bound by the bytes of
+ *   the weights it streams, 1/32 of fp32 when packed.
+ *   "Architecture Decision Record" (Binary-Neural-Networks lab), Decision:
+ *   matmuls are inferred with a packed XNOR/XOR + popcount kernel
+ *   (binary_gemm_u64); this library is that operation for gfx950.
+ *   "Encoder / decoder" (bnn/seq API), BinaryAutoEncoder: binary layers run
+ *   back to back, which bnn_gemm_sign_repack serves by emitting the packed
+ *   input of the next binary layer.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  X is M x K (activations, one row per token), W is N x K (one row
+ * per output channel, nn.Linear orientation), Y = X * W^T is M x N.  All
+ * matrices are dense row-major.  A packed matrix with R rows and K logical
+ * columns is R x bnn_words(K) uint64 words, contiguous; logical element k
+ * of a row is bit (k % 64) of word (k / 64), least significant bit first,
+ * words little-endian in memory.
+ *
+ * Memory.  Every pointer is a DEVICE pointer owned by the caller.  The
+ * library allocates nothing, frees nothing, keeps no state between calls
+ * and never synchronizes: each call enqueues its kernels on `stream` (a
+ * hipStream_t; NULL means the default stream) and returns.  Inputs and
+ * outputs must not overlap.
+ *
+ * Pad bits.  Outputs that are packed (bnn_pack_signs, bnn_gemm_sign_repack)
+ * have every pad bit 0 (+1).  Packed INPUTS may hold anything in their pad
+ * bits: the kernels mask the last word, so only the K logical bits count.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued;
+ * on error nothing is written or launched and a non-zero bnn_status is
+ * returned.  A pointer may be NULL only when the buffer it names has no
+ * elements.  M = 0 or N = 0 returns BNN_OK without a launch.  K = 0 is valid
+ * and launches (dots are 0).  Dimensions must be >= 0 and < 2^31.  A launch
+ * failure reported by the HIP runtime right after the launch returns
+ * BNN_E_LAUNCH; faults during execution surface at the caller's next
+ * synchronization, as for any HIP kernel.
+ *
+ * Thread safety.  Calls are re-entrant and may be issued from several host
+ * threads and on several streams at once.
+ */
+#ifndef BNN_H_
+#define BNN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bnn_status {
+  BNN_OK = 0,
+  BNN_E_NULL = 1,   /* NULL pointer for a non-empty buffer */
+  BNN_E_SHAPE = 2,  /* negative or too large dimension, ld < k, ... */
+  BNN_E_DTYPE = 3,  /* unknown element type */
+  BNN_E_ALIGN = 4,  /* pointer not aligned to its element size */
+  BNN_E_LAUNCH = 5, /* the HIP runtime rejected a kernel launch */
+  BNN_E_ARG = 6     /* unknown epilogue or algorithm selector */
+} bnn_status;
+
+typedef enum bnn_dtype {
+  BNN_FP32 = 0, /* IEEE binary32 */
+  BNN_BF16 = 1  /* bfloat16, the upper 16 bits of a binary32 */
+} bnn_dtype;
+
+/* Output stage of a product (see bnn_gemm_ex). */
+typedef enum bnn_epilogue {
+  BNN_EPI_I32 = 0,    /* int32 y = K - 2d */
+  BNN_EPI_SCALED = 1, /* fp32 y = (float)(K - 2d) * alpha[n] */
+  BNN_EPI_REPACK = 2  /* packed sign of (K - 2d) along N */
+} bnn_epilogue;
+
+/* Kernel family (see bnn_gemm_ex).  AUTO picks by shape. */
+typedef enum bnn_algo {
+  BNN_ALGO_AUTO = 0,  /* GEMV for small M, tiled GEMM otherwise */
+  BNN_ALGO_GEMV = 1,  /* weight-streaming kernel; any M, fastest at M <= 8 */
+  BNN_ALGO_TILED = 2  /* LDS-tiled XOR + popcount GEMM */
+} bnn_algo;
+
+/* ceil(k / 64): 64-bit words per packed row of k logical values; 0 for
+ * k <= 0.  ("Binary Math Effectiveness", section 2.1.) */
+int64_t bnn_words(int64_t k);
+
+/* Static, NUL-terminated description of a status code. */
+const char *bnn_status_str(int status);
+
+/* Static version string of the library. */
+const char *bnn_version(void);
+
+/*
+ * bnn_pack_signs -- sign-project and pack along K.
+ * ("Binary Math Effectiveness", section 1: encoding table and the edge-case
+ * rows "padding" and "non-+-1 inputs".)
+ *
+ *   src     rows x ld_src elements of type `dtype` (BNN_FP32 or BNN_BF16),
+ *           row-major; only the first k elements of each row are read.
+ *   rows    number of rows (>= 0).
+ *   k       logical row length (>= 0).
+ *   ld_src  row stride of src in ELEMENTS (>= k).
+ *   dst     rows x bnn_words(k) uint64 output, 8-byte aligned.
+ *
+ * Element v becomes bit 1 (-1) unless v > 0, in which case it becomes bit 0
+ * (+1): +0, -0 and NaN give bit 1, positive subnormals give bit 0 (the test
+ * is done on the bit pattern, so no flush-to-zero applies).  Pad bits of
+ * each row's last word are written as 0.
+ * Errors: BNN_E_NULL, BNN_E_SHAPE (negative sizes, ld_src < k),
+ * BNN_E_DTYPE, BNN_E_ALIGN (src not aligned to its element, dst not 8-byte
+ * aligned), BNN_E_LAUNCH.
+ */
+bnn_status bnn_pack_signs(const void *src, int dtype, int64_t rows, int64_t k, int64_t ld_src,
+                          uint64_t *dst, void *stream);
+
+/*
+ * bnn_gemm_u64 -- y[m][n] = <x_m, w_n> = K - 2 * popcount(x_m XOR w_n) over
+ * the K logical bits.  ("Binary Math Effectiveness", section 1, the core
+ * identity and its edge cases; "Architecture Decision Record", Decision.)
+ *
+ *   xp  M x bnn_words(K) packed activations, 8-byte aligned.
+ *   wp  N x bnn_words(K) packed weights, 8-byte aligned.
+ *   y   M x N int32 output, row-major, 4-byte aligned.
+ * K = 0 gives y = 0.  Errors: BNN_E_NULL, BNN_E_SHAPE, BNN_E_ALIGN,
+ * BNN_E_LAUNCH.
+ */
+bnn_status bnn_gemm_u64(const uint64_t *xp, const uint64_t *wp, int32_t *y, int64_t M, int64_t N,
+                        int64_t K, void *stream);
+
+/*
+ * bnn_gemm_u64_scaled -- y[m][n] = (float)(K - 2d) * alpha[n], one fp32
+ * multiply rounded to nearest even (the integer converts exactly while
+ * |K - 2d| <= 2^24).  ("Binary Math Effectiveness", section 1, edge case
+ * "channel scale alpha"; alpha = 0 gives 0.)
+ *
+ *   alpha  N fp32 per-output-channel scales, 4-byte aligned.
+ *   y      M x N fp32 output, row-major, 4-byte aligned.
+ * Other arguments and errors as bnn_gemm_u64.
+ */
+bnn_status bnn_gemm_u64_scaled(const uint64_t *xp, const uint64_t *wp, const float *alpha,
+                               float *y, int64_t M, int64_t N, int64_t K, void *stream);
+
+/*
+ * bnn_gemm_sign_repack -- the packed input of the next binary layer:
+ * bit n of output row m is 1 (-1) when K - 2d <= 0 and 0 (+1) otherwise,
+ * packed along N exactly as bnn_pack_signs packs along K.  ("Binary Math
+ * Effectiveness", section 1, the projection rule applied to a layer's
+ * integer output; "Encoder / decoder", BinaryAutoEncoder, for chained
+ * binary layers.)
+ *
+ *   yp  M x bnn_words(N) uint64 output, 8-byte aligned; pad bits are 0.
+ * K = 0 gives dots of 0 and hence every logical bit 1.  Other arguments and
+ * errors as bnn_gemm_u64.
+ */
+bnn_status bnn_gemm_sign_repack(const uint64_t *xp, const uint64_t *wp, uint64_t *yp, int64_t M,
+                                int64_t N, int64_t K, void *stream);
+
+/*
+ * bnn_gemm_ex -- the general form of the three products above, with an
+ * explicit kernel family.  `y` is int32*, float* or uint64* according to
+ * `epilogue` (BNN_EPI_*); `alpha` is read only for BNN_EPI_SCALED.  `algo`
+ * is a BNN_ALGO_* value; every family gives bit-identical results, so the
+ * selector only changes speed.  Errors as above, plus BNN_E_ARG for an
+ * unknown epilogue or algo.
+ */
+bnn_status bnn_gemm_ex(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+                       int64_t M, int64_t N, int64_t K, int epilogue, int algo, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BNN_H_ */

@@ -1,0 +1,188 @@
+"""packed_xor_popcount_amd -- Python binding of libbnn.so (include/bnn.h).
+
+Packed binary (+1/-1) matrix products on MI355X (gfx950): sign projection and
+packing along K, and <x, w> = K - 2 * popcount(x XOR w) with int32,
+alpha-scaled fp32 or sign -> repack outputs ("Binary Math Effectiveness --
+why / how / when", section 1).
+
+This module only marshals arguments: it checks tensor devices, dtypes and
+shapes, allocates outputs with PyTorch (device memory is PyTorch's; the
+library allocates nothing), and passes raw device pointers and the current
+HIP stream to the C entry points of the same names.  Every step of the
+computation runs in the HIP kernels of libbnn.so; there is no CPU path.  If
+libbnn.so is missing this module raises instead of falling back.
+
+Packed matrices are ``torch.int64`` tensors of shape ``(rows, words(K))``
+holding the uint64 words bit for bit (bit k%64 of word k/64 is element k,
+least significant bit first; bit 1 means -1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BnnError", "EPI_I32", "EPI_SCALED", "EPI_REPACK", "ALGO_AUTO", "ALGO_GEMV", "ALGO_TILED",
+    "library", "library_path", "words", "pack_signs", "gemm_u64", "gemm_u64_scaled",
+    "gemm_sign_repack", "gemm_ex", "version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libbnn.so")
+
+BNN_FP32, BNN_BF16 = 0, 1
+EPI_I32, EPI_SCALED, EPI_REPACK = 0, 1, 2
+ALGO_AUTO, ALGO_GEMV, ALGO_TILED = 0, 1, 2
+
+EXPORTED = ("bnn_words", "bnn_status_str", "bnn_version", "bnn_pack_signs", "bnn_gemm_u64",
+            "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex")
+
+
+class BnnError(RuntimeError):
+    """A non-zero bnn_status returned by libbnn.so."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def library():
+    """The loaded libbnn.so (built in-tree first if it does not exist yet)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(library_path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.bnn_words.argtypes, lib.bnn_words.restype = [I64], I64
+    lib.bnn_status_str.argtypes, lib.bnn_status_str.restype = [I], ctypes.c_char_p
+    lib.bnn_version.argtypes, lib.bnn_version.restype = [], ctypes.c_char_p
+    lib.bnn_pack_signs.argtypes = [P, I, I64, I64, I64, P, P]
+    lib.bnn_gemm_u64.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.bnn_gemm_u64_scaled.argtypes = [P, P, P, P, I64, I64, I64, P]
+    lib.bnn_gemm_sign_repack.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.bnn_gemm_ex.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
+    for name in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack",
+                 "bnn_gemm_ex"):
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def _status_str(status: int) -> str:
+    return library().bnn_status_str(int(status)).decode()
+
+
+def version() -> str:
+    return library().bnn_version().decode()
+
+
+def words(k: int) -> int:
+    """ceil(k/64): 64-bit words per packed row of k logical values."""
+    return int(library().bnn_words(int(k)))
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise BnnError(status, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_cuda(name: str, t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+
+
+def _packed(name: str, t: torch.Tensor, k: int) -> int:
+    _need_cuda(name, t)
+    if t.dtype != torch.int64 or t.dim() != 2 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous 2-D int64 tensor of packed words")
+    if t.shape[1] != words(k):
+        raise ValueError(f"{name} has {t.shape[1]} words per row, K={k} needs {words(k)}")
+    return t.shape[0]
+
+
+def pack_signs(src: torch.Tensor, k: int | None = None, out: torch.Tensor | None = None):
+    """Sign-project and pack a 2-D fp32 or bf16 CUDA tensor along its last
+    dimension (the first ``k`` columns, default all).  Rows may be strided
+    (``src.stride(1)`` must be 1).  Returns int64 ``(rows, words(k))``."""
+    _need_cuda("src", src)
+    if src.dim() != 2 or (src.shape[1] > 1 and src.stride(1) != 1):
+        raise ValueError("src must be 2-D with unit stride along its last dimension")
+    if src.dtype == torch.float32:
+        dt = BNN_FP32
+    elif src.dtype == torch.bfloat16:
+        dt = BNN_BF16
+    else:
+        raise TypeError("src must be float32 or bfloat16")
+    rows, cols = src.shape
+    k = cols if k is None else int(k)
+    ld = src.stride(0) if rows > 1 else max(cols, 1)
+    if out is None:
+        out = torch.empty((rows, words(k)), dtype=torch.int64, device=src.device)
+    else:
+        _packed("out", out, k)
+    st = library().bnn_pack_signs(_ptr(src), dt, rows, k, ld, _ptr(out), _stream(src))
+    _check(st, "bnn_pack_signs")
+    return out
+
+
+def gemm_ex(xp: torch.Tensor, wp: torch.Tensor, K: int, epilogue: int = EPI_I32,
+            algo: int = ALGO_AUTO, alpha: torch.Tensor | None = None,
+            out: torch.Tensor | None = None):
+    """General packed product (bnn_gemm_ex): int32 (EPI_I32), alpha-scaled
+    fp32 (EPI_SCALED) or packed signs (EPI_REPACK), with an explicit kernel
+    family (ALGO_AUTO, ALGO_GEMV, ALGO_TILED)."""
+    M = _packed("xp", xp, K)
+    N = _packed("wp", wp, K)
+    if wp.device != xp.device:
+        raise ValueError("xp and wp must be on the same device")
+    if epilogue == EPI_SCALED:
+        _need_cuda("alpha", alpha)
+        if alpha.dtype != torch.float32 or alpha.shape != (N,) or not alpha.is_contiguous():
+            raise ValueError("alpha must be a contiguous float32 tensor of shape (N,)")
+    if epilogue == EPI_I32:
+        shape, dtype = (M, N), torch.int32
+    elif epilogue == EPI_SCALED:
+        shape, dtype = (M, N), torch.float32
+    elif epilogue == EPI_REPACK:
+        shape, dtype = (M, words(N)), torch.int64
+    else:
+        raise ValueError(f"unknown epilogue {epilogue}")
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=xp.device)
+    elif tuple(out.shape) != shape or out.dtype != dtype or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} tensor of shape {shape}")
+    st = library().bnn_gemm_ex(_ptr(xp), _ptr(wp), _ptr(alpha) if epilogue == EPI_SCALED else None,
+                               _ptr(out), M, N, int(K), int(epilogue), int(algo), _stream(xp))
+    _check(st, "bnn_gemm_ex")
+    return out
+
+
+def gemm_u64(xp, wp, K, out=None):
+    """int32 ``(M, N)``: ``<x_m, w_n> = K - 2 * popcount(x_m XOR w_n)``."""
+    return gemm_ex(xp, wp, K, EPI_I32, ALGO_AUTO, None, out)
+
+
+def gemm_u64_scaled(xp, wp, alpha, K, out=None):
+    """fp32 ``(M, N)``: ``(float)<x_m, w_n> * alpha[n]``."""
+    return gemm_ex(xp, wp, K, EPI_SCALED, ALGO_AUTO, alpha, out)
+
+
+def gemm_sign_repack(xp, wp, K, out=None):
+    """int64 ``(M, words(N))``: projected signs of ``<x_m, w_n>`` packed along N."""
+    return gemm_ex(xp, wp, K, EPI_REPACK, ALGO_AUTO, None, out)

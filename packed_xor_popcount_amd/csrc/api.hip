@@ -1,0 +1,90 @@
+// api.hip -- the C-ABI of libbnn.so: host-side validation, kernel choice and
+// status codes.  Every check runs before anything is enqueued, so an invalid
+// call writes nothing and launches nothing.  No allocation, no
+// synchronization, no state.
+#include "../../include/bnn.h"
+#include "bnn_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;  // M, N, K, rows and ld limits
+constexpr int64_t kGemvMaxM = 8;               // AUTO picks the GEMV kernel up to here
+
+bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p) % a != 0; }
+
+bnn_status launch_status(hipError_t e) { return e == hipSuccess ? BNN_OK : BNN_E_LAUNCH; }
+
+bnn_status check_gemm(const uint64_t *xp, const uint64_t *wp, const float *alpha, const void *y,
+                      int64_t M, int64_t N, int64_t K, int epilogue, int algo) {
+  if (epilogue < BNN_EPI_I32 || epilogue > BNN_EPI_REPACK) return BNN_E_ARG;
+  if (algo < BNN_ALGO_AUTO || algo > BNN_ALGO_TILED) return BNN_E_ARG;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return BNN_E_SHAPE;
+  const int64_t kw = bnn_words(K);
+  if ((M * kw > 0 && !xp) || (N * kw > 0 && !wp) || (M * N > 0 && !y)) return BNN_E_NULL;
+  if (epilogue == BNN_EPI_SCALED && M * N > 0 && !alpha) return BNN_E_NULL;
+  if (misaligned(xp, 8) || misaligned(wp, 8)) return BNN_E_ALIGN;
+  if (misaligned(y, epilogue == BNN_EPI_REPACK ? 8 : 4)) return BNN_E_ALIGN;
+  if (epilogue == BNN_EPI_SCALED && misaligned(alpha, 4)) return BNN_E_ALIGN;
+  return BNN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bnn_words(int64_t k) { return k <= 0 ? 0 : (k + 63) / 64; }
+
+const char *bnn_status_str(int status) {
+  switch (status) {
+    case BNN_OK: return "ok";
+    case BNN_E_NULL: return "null pointer for a non-empty buffer";
+    case BNN_E_SHAPE: return "invalid shape (negative, too large, or ld < k)";
+    case BNN_E_DTYPE: return "unknown element type";
+    case BNN_E_ALIGN: return "pointer not aligned to its element size";
+    case BNN_E_LAUNCH: return "kernel launch failed";
+    case BNN_E_ARG: return "unknown epilogue or algorithm selector";
+    default: return "unknown status";
+  }
+}
+
+const char *bnn_version(void) { return "bnn-mi355x 0.1 (gfx950)"; }
+
+bnn_status bnn_pack_signs(const void *src, int dtype, int64_t rows, int64_t k, int64_t ld_src,
+                          uint64_t *dst, void *stream) {
+  if (dtype != BNN_FP32 && dtype != BNN_BF16) return BNN_E_DTYPE;
+  if (rows < 0 || k < 0 || ld_src < k || rows >= kMaxDim || ld_src >= kMaxDim) return BNN_E_SHAPE;
+  if (rows * k > 0 && !src) return BNN_E_NULL;
+  if (rows * bnn_words(k) > 0 && !dst) return BNN_E_NULL;
+  if (misaligned(src, dtype == BNN_FP32 ? 4 : 2) || misaligned(dst, 8)) return BNN_E_ALIGN;
+  if (rows == 0 || k == 0) return BNN_OK;
+  return launch_status(
+      bnn::launch_pack(src, dtype, rows, k, ld_src, dst, static_cast<hipStream_t>(stream)));
+}
+
+bnn_status bnn_gemm_ex(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+                       int64_t M, int64_t N, int64_t K, int epilogue, int algo, void *stream) {
+  const bnn_status st = check_gemm(xp, wp, alpha, y, M, N, K, epilogue, algo);
+  if (st != BNN_OK) return st;
+  if (M == 0 || N == 0) return BNN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool gemv = algo == BNN_ALGO_GEMV || (algo == BNN_ALGO_AUTO && M <= kGemvMaxM);
+  if (gemv) return launch_status(bnn::launch_gemv(xp, wp, alpha, y, M, N, K, epilogue, s));
+  return launch_status(bnn::launch_gemm_tiled(xp, wp, alpha, y, M, N, K, epilogue, s));
+}
+
+bnn_status bnn_gemm_u64(const uint64_t *xp, const uint64_t *wp, int32_t *y, int64_t M, int64_t N,
+                        int64_t K, void *stream) {
+  return bnn_gemm_ex(xp, wp, nullptr, y, M, N, K, BNN_EPI_I32, BNN_ALGO_AUTO, stream);
+}
+
+bnn_status bnn_gemm_u64_scaled(const uint64_t *xp, const uint64_t *wp, const float *alpha,
+                               float *y, int64_t M, int64_t N, int64_t K, void *stream) {
+  return bnn_gemm_ex(xp, wp, alpha, y, M, N, K, BNN_EPI_SCALED, BNN_ALGO_AUTO, stream);
+}
+
+bnn_status bnn_gemm_sign_repack(const uint64_t *xp, const uint64_t *wp, uint64_t *yp, int64_t M,
+                                int64_t N, int64_t K, void *stream) {
+  return bnn_gemm_ex(xp, wp, nullptr, yp, M, N, K, BNN_EPI_REPACK, BNN_ALGO_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// bnn_internal.h -- declarations shared by the HIP translation units of
+// libbnn.so (kernel launchers and small device helpers).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bnn {
+
+// Launchers: each enqueues its kernel(s) on `s` and returns hipGetLastError().
+// Arguments are already validated by the C-ABI layer.
+hipError_t launch_pack(const void *src, int dtype, int64_t rows, int64_t k, int64_t ld,
+                       uint64_t *dst, hipStream_t s);
+
+hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+                             int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
+
+hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+                       int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
+
+// Mask of the logical bits of a row's last 64-bit word.
+__host__ __device__ inline uint64_t tail_mask(int64_t k) {
+  const int r = (int)(k & 63);
+  return r ? ((uint64_t(1) << r) - 1) : ~uint64_t(0);
+}
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+}  // namespace bnn

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: libbnn.so loads, exports every entry point
+include/bnn.h declares, and rejects invalid arguments on the host before any
+launch (so these calls never reach the device)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import packed_xor_popcount_amd as bnn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bnn.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_LAUNCH, E_ARG = range(7)
+P = ctypes.c_void_p
+FAKE = P(0x1000)        # aligned, never dereferenced: every call below fails validation
+FAKE_ODD = P(0x1003)    # misaligned
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bnn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bnn.library()
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for s in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack"):
+        assert s in syms
+    assert set(syms) == set(bnn.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bnn.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)", out))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(lib, s)
+
+
+def test_library_is_gfx950_code():
+    # the offload target triple of the embedded device code object
+    with open(bnn.library_path, "rb") as f:
+        blob = f.read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_words_and_strings(lib):
+    for k in (-5, 0, 1, 63, 64, 65, 1000, 4096, 2 ** 31):
+        assert bnn.words(k) == (0 if k <= 0 else -(-k // 64))
+    for s in range(7):
+        assert lib.bnn_status_str(s)
+    assert b"unknown" in lib.bnn_status_str(99)
+    assert "gfx950" in bnn.version()
+
+
+def test_pack_validation(lib):
+    f = lib.bnn_pack_signs
+    assert f(FAKE, 7, 1, 1, 1, FAKE, None) == E_DTYPE
+    assert f(FAKE, 0, -1, 1, 1, FAKE, None) == E_SHAPE
+    assert f(FAKE, 0, 1, -1, 1, FAKE, None) == E_SHAPE
+    assert f(FAKE, 0, 2, 10, 9, FAKE, None) == E_SHAPE        # ld < k
+    assert f(FAKE, 0, 2 ** 30, 1, 1, FAKE, None) == E_SHAPE    # too many rows
+    assert f(None, 0, 2, 10, 10, FAKE, None) == E_NULL
+    assert f(FAKE, 0, 2, 10, 10, None, None) == E_NULL
+    assert f(FAKE_ODD, 0, 2, 10, 10, FAKE, None) == E_ALIGN   # fp32 needs 4 B
+    assert f(P(0x1002), 1, 2, 10, 10, P(0x1004), None) == E_ALIGN  # dst needs 8 B
+    # empty inputs: OK, nothing launched, NULL allowed
+    assert f(None, 0, 0, 10, 10, None, None) == OK
+    assert f(None, 1, 5, 0, 0, None, None) == OK
+
+
+def test_gemm_validation(lib):
+    g = lib.bnn_gemm_ex
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 3, 0, None) == E_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 0, 9, None) == E_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, -1, 1, 1, 0, 0, None) == E_SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, -1, 1, 0, 0, None) == E_SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, -1, 0, 0, None) == E_SHAPE
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, 2 ** 30, 0, 0, None) == E_SHAPE
+    assert g(None, FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, None) == E_NULL
+    assert g(FAKE, None, FAKE, FAKE, 1, 1, 1, 0, 0, None) == E_NULL
+    assert g(FAKE, FAKE, FAKE, None, 1, 1, 1, 0, 0, None) == E_NULL
+    assert g(FAKE, FAKE, None, FAKE, 1, 1, 1, 1, 0, None) == E_NULL   # scaled needs alpha
+    assert g(FAKE_ODD, FAKE, FAKE, FAKE, 1, 1, 1, 0, 0, None) == E_ALIGN
+    assert g(FAKE, FAKE_ODD, FAKE, FAKE, 1, 1, 1, 0, 0, None) == E_ALIGN
+    assert g(FAKE, FAKE, FAKE, P(0x1002), 1, 1, 1, 0, 0, None) == E_ALIGN
+    assert g(FAKE, FAKE, FAKE, P(0x1004), 1, 1, 1, 2, 0, None) == E_ALIGN  # repack words: 8 B
+    assert g(FAKE, FAKE, P(0x1001), FAKE, 1, 1, 1, 1, 0, None) == E_ALIGN
+    # the named entry points validate the same way
+    assert lib.bnn_gemm_u64(None, FAKE, FAKE, 1, 1, 1, None) == E_NULL
+    assert lib.bnn_gemm_u64_scaled(FAKE, FAKE, None, FAKE, 1, 1, 1, None) == E_NULL
+    assert lib.bnn_gemm_sign_repack(FAKE, FAKE, FAKE_ODD, 1, 1, 1, None) == E_ALIGN
+    # empty products: OK without a launch, NULLs allowed for empty buffers
+    assert g(None, FAKE, None, None, 0, 5, 64, 0, 0, None) == OK
+    assert g(FAKE, None, None, None, 5, 0, 64, 1, 0, None) == OK
+    assert g(None, None, None, None, 0, 0, 64, 2, 0, None) == OK
+    assert lib.bnn_gemm_u64(None, None, None, 0, 0, 0, None) == OK
+    # a buffer with elements may not be NULL even when the product is empty
+    assert g(None, None, None, None, 0, 5, 64, 0, 0, None) == E_NULL
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        bnn.pack_signs(torch.zeros(2, 3))
+    with pytest.raises(TypeError):
+        bnn.gemm_u64(torch.zeros(2, 1, dtype=torch.int64), torch.zeros(2, 1, dtype=torch.int64), 3)

@@ -1,0 +1,309 @@
+"""GPU parity: every HIP kernel behind include/bnn.h against the CPU oracle,
+element by element, on the same seeded inputs.
+
+Bar: packed words and int32 outputs bit-exact; alpha-scaled fp32 within
+1e-6 relative (the bar the workload statement sets) -- and in fact
+bit-identical, since both sides take one round-to-nearest-even fp32 product
+of the same exactly converted integer; zeros compare by value (+0 == -0).
+
+Sizes span several tiles and ragged tails (tile = 32 rows x 256 columns x
+8 words for the tiled kernel; 64 columns per step for the GEMV kernel);
+every kernel family is forced explicitly through bnn_gemm_ex, and the named
+entry points are checked with their automatic choice.  The full-size
+workloads are checked in the launch configuration the benchmark times, on
+outputs the oracle computes one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import packed_xor_popcount_amd as bnn
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ALGOS = [bnn.ALGO_GEMV, bnn.ALGO_TILED, bnn.ALGO_AUTO]
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev_words(p: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(p, dtype=np.uint64).view(np.int64)).to(DEV)
+
+
+def words_np(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint64)
+
+
+def host_input(x: torch.Tensor) -> np.ndarray:
+    """The exact bytes the oracle packs: fp32 values or bf16 bit patterns."""
+    return workloads.bf16_bits(x) if x.dtype == torch.bfloat16 else x.numpy()
+
+
+def assert_scaled_equal(got: np.ndarray, ref: np.ndarray):
+    assert got.shape == ref.shape and got.dtype == np.float32
+    nz = ref != 0
+    rel = np.abs(got[nz].astype(np.float64) - ref[nz]) / np.abs(ref[nz].astype(np.float64))
+    assert rel.size == 0 or rel.max() <= 1e-6
+    assert np.array_equal(got[nz].view(np.uint32), ref[nz].view(np.uint32))
+    assert np.all(got[~nz] == 0)
+
+
+def rand_packed(rng, rows, k, garbage=True):
+    """Random packed rows; optionally with garbage in the pad bits, which
+    every product must ignore."""
+    kw = oracle.words(k)
+    p = rng.integers(0, 2 ** 64, size=(rows, kw), dtype=np.uint64)
+    if kw and k % 64:
+        keep = np.uint64((1 << (k % 64)) - 1)
+        clean = p.copy()
+        clean[:, -1] &= keep
+        return (p if garbage else clean), clean
+    return p, p
+
+
+# ---------------------------------------------------------------------------
+# bnn_pack_signs
+
+
+@pytest.mark.parametrize("rows,k", [(1, 1), (1, 63), (3, 64), (5, 65), (7, 1000), (64, 4096),
+                                    (130, 333), (1000, 129), (2, 5000), (4097, 40)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pack_parity(rows, k, dtype):
+    say("pack", rows, k, dtype)
+    g = workloads.generator(rows * 7919 + k)
+    x = workloads.plant_zeros(g, workloads.normal(g, rows, k), 0.02) if rows * k >= 2 else \
+        workloads.normal(g, rows, k)
+    x = x.to(dtype)
+    got = words_np(bnn.pack_signs(x.to(DEV)))
+    ref = oracle.pack(host_input(x))
+    assert np.array_equal(got, ref)
+
+
+def test_pack_projection_tables():
+    from tests import _golden
+    f32 = np.array([b for b, _, _ in _golden.projection_f32()], dtype=np.uint32)
+    exp = np.array([bit for _, _, bit in _golden.projection_f32()], dtype=np.uint64)
+    x = torch.from_numpy(f32.view(np.float32).reshape(1, -1).copy())
+    got = words_np(bnn.pack_signs(x.to(DEV)))[0, 0]
+    assert got == np.sum(exp << np.arange(exp.size, dtype=np.uint64))
+    b16 = np.array([b for b, _, _ in _golden.projection_bf16()], dtype=np.uint16)
+    exp = np.array([bit for _, _, bit in _golden.projection_bf16()], dtype=np.uint64)
+    x = torch.from_numpy(b16.view(np.int16).reshape(1, -1).copy()).view(torch.bfloat16)
+    got = words_np(bnn.pack_signs(x.to(DEV)))[0, 0]
+    assert got == np.sum(exp << np.arange(exp.size, dtype=np.uint64))
+
+
+def test_pack_strided_rows_and_prefix():
+    g = workloads.generator(77)
+    big = workloads.normal(g, 33, 300).to(DEV)
+    view = big[:, 10:210]                       # row stride 300, 200 columns
+    got = words_np(bnn.pack_signs(view, k=150))  # first 150 of them
+    ref = oracle.pack(np.ascontiguousarray(big.cpu().numpy()[:, 10:160]))
+    assert np.array_equal(got, ref)
+
+
+def test_pack_empty():
+    assert bnn.pack_signs(torch.empty(0, 10, device=DEV)).shape == (0, 1)
+    assert bnn.pack_signs(torch.empty(4, 0, device=DEV)).shape == (4, 0)
+
+
+# ---------------------------------------------------------------------------
+# products, every kernel family, ragged shapes, garbage pad bits
+
+SHAPES = [
+    (1, 1, 1), (1, 5, 0), (3, 64, 64), (1, 256, 512), (2, 300, 65), (8, 1000, 1000),
+    (9, 65, 127), (33, 257, 129), (64, 1000, 1000), (65, 513, 4095), (100, 64, 8192),
+    (31, 255, 63), (256, 256, 512), (5, 1025, 3000), (40, 130, 2049),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("algo", ALGOS)
+def test_gemm_all_epilogues(M, N, K, algo):
+    say("gemm", M, N, K, "algo", algo)
+    rng = np.random.default_rng(M * 1000003 + N * 1009 + K)
+    xg, xc = rand_packed(rng, M, K)
+    wg, wc = rand_packed(rng, N, K)
+    alpha = (rng.standard_normal(N) * 3).astype(np.float32)
+    alpha[::5] = 0.0
+    xd, wd, ad = to_dev_words(xg), to_dev_words(wg), torch.from_numpy(alpha).to(DEV)
+
+    ref = oracle.gemm_i32(xc, wc, K)
+    got = bnn.gemm_ex(xd, wd, K, bnn.EPI_I32, algo).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+    refs = oracle.gemm_scaled(xc, wc, alpha, K)
+    gots = bnn.gemm_ex(xd, wd, K, bnn.EPI_SCALED, algo, alpha=ad).cpu().numpy()
+    assert_scaled_equal(gots, refs)
+
+    refp = oracle.sign_repack(xc, wc, K)
+    gotp = words_np(bnn.gemm_ex(xd, wd, K, bnn.EPI_REPACK, algo))
+    assert np.array_equal(gotp, refp)
+
+
+def test_named_entry_points_match_oracle():
+    rng = np.random.default_rng(5)
+    for M, N, K in [(1, 777, 1000), (200, 300, 700)]:
+        xg, xc = rand_packed(rng, M, K)
+        wg, wc = rand_packed(rng, N, K)
+        alpha = rng.standard_normal(N).astype(np.float32)
+        xd, wd = to_dev_words(xg), to_dev_words(wg)
+        assert np.array_equal(bnn.gemm_u64(xd, wd, K).cpu().numpy(), oracle.gemm_i32(xc, wc, K))
+        assert_scaled_equal(bnn.gemm_u64_scaled(xd, wd, torch.from_numpy(alpha).to(DEV), K)
+                            .cpu().numpy(), oracle.gemm_scaled(xc, wc, alpha, K))
+        assert np.array_equal(words_np(bnn.gemm_sign_repack(xd, wd, K)),
+                              oracle.sign_repack(xc, wc, K))
+
+
+def test_k_zero_and_empty_products():
+    for algo in ALGOS:
+        xd = torch.empty(64, 0, dtype=torch.int64, device=DEV)
+        wd = torch.empty(1000, 0, dtype=torch.int64, device=DEV)
+        y = bnn.gemm_ex(xd, wd, 0, bnn.EPI_I32, algo)
+        assert y.shape == (64, 1000) and not y.any()
+        a = torch.randn(1000, device=DEV)
+        assert not bnn.gemm_ex(xd, wd, 0, bnn.EPI_SCALED, algo, alpha=a).any()
+        p = words_np(bnn.gemm_ex(xd, wd, 0, bnn.EPI_REPACK, algo))
+        assert np.all(p[:, :15] == np.uint64(0xFFFFFFFFFFFFFFFF))
+        assert np.all(p[:, 15] == np.uint64(0x000000FFFFFFFFFF))
+    e = torch.empty(0, 2, dtype=torch.int64, device=DEV)
+    w = torch.zeros(3, 2, dtype=torch.int64, device=DEV)
+    assert bnn.gemm_u64(e, w, 100).shape == (0, 3)
+    assert bnn.gemm_u64(w, e, 100).shape == (3, 0)
+
+
+def test_large_k():
+    # K ~ 1M bits: long K loops, int32 range, last word 3 bits wide
+    rng = np.random.default_rng(9)
+    M, N, K = 3, 70, 1_000_003
+    xg, xc = rand_packed(rng, M, K)
+    wg, wc = rand_packed(rng, N, K)
+    ref = oracle.gemm_i32(xc, wc, K)
+    for algo in ALGOS:
+        got = bnn.gemm_ex(to_dev_words(xg), to_dev_words(wg), K, bnn.EPI_I32, algo).cpu().numpy()
+        assert np.array_equal(got, ref)
+
+
+def test_unaligned_16b_operands_use_narrow_loads():
+    # 8-byte aligned but not 16-byte aligned operands (views starting at word 1)
+    rng = np.random.default_rng(10)
+    M, N, K = 2, 100, 256
+    xg, xc = rand_packed(rng, M, K)
+    wg, wc = rand_packed(rng, N, K)
+    xbig = to_dev_words(np.concatenate([np.zeros(1, np.uint64), xg.ravel()]))
+    wbig = to_dev_words(np.concatenate([np.zeros(1, np.uint64), wg.ravel()]))
+    xd = xbig[1:].view(M, oracle.words(K))
+    wd = wbig[1:].view(N, oracle.words(K))
+    assert xd.data_ptr() % 16 == 8
+    got = bnn.gemm_ex(xd, wd, K, bnn.EPI_I32, bnn.ALGO_GEMV).cpu().numpy()
+    assert np.array_equal(got, oracle.gemm_i32(xc, wc, K))
+
+
+def test_runs_on_a_side_stream():
+    rng = np.random.default_rng(12)
+    xg, xc = rand_packed(rng, 40, 300)
+    wg, wc = rand_packed(rng, 50, 300)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = bnn.gemm_u64(to_dev_words(xg), to_dev_words(wg), 300)
+    s.synchronize()
+    assert np.array_equal(y.cpu().numpy(), oracle.gemm_i32(xc, wc, 300))
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+
+
+def test_workload_gemv_small():
+    d = workloads.make("gemv_small")
+    xp = bnn.pack_signs(d["x"].to(DEV))
+    wp = bnn.pack_signs(d["w"].to(DEV))
+    rx, rw = oracle.pack(d["x"].numpy()), oracle.pack(d["w"].numpy())
+    assert np.array_equal(words_np(xp), rx) and np.array_equal(words_np(wp), rw)
+    assert np.array_equal(bnn.gemm_u64(xp, wp, d["K"]).cpu().numpy(), oracle.gemm_i32(rx, rw, d["K"]))
+
+
+def test_workload_gemv_4096():
+    d = workloads.make("gemv_4096")
+    xp = bnn.pack_signs(d["x"].to(DEV))
+    wp = bnn.pack_signs(d["w"].to(DEV))
+    rx, rw = oracle.pack(workloads.bf16_bits(d["x"])), oracle.pack(d["w"].numpy())
+    assert np.array_equal(words_np(xp), rx) and np.array_equal(words_np(wp), rw)
+    alpha = d["alpha"].numpy()
+    got = bnn.gemm_u64_scaled(xp, wp, d["alpha"].to(DEV), d["K"]).cpu().numpy()
+    assert_scaled_equal(got, oracle.gemm_scaled(rx, rw, alpha, d["K"]))
+
+
+def test_workload_edge_1000():
+    d = workloads.make("edge_1000")
+    K = d["K"]
+    xp = bnn.pack_signs(d["x"].to(DEV))
+    wp = bnn.pack_signs(d["w"].to(DEV))
+    rx, rw = oracle.pack(d["x"].numpy()), oracle.pack(d["w"].numpy())
+    assert np.array_equal(words_np(xp), rx) and np.array_equal(words_np(wp), rw)
+    assert np.array_equal(bnn.gemm_u64(xp, wp, K).cpu().numpy(), oracle.gemm_i32(rx, rw, K))
+    alpha = d["alpha"].numpy()
+    assert (alpha[::10] == 0).all()
+    got = bnn.gemm_u64_scaled(xp, wp, d["alpha"].to(DEV), K).cpu().numpy()
+    assert_scaled_equal(got, oracle.gemm_scaled(rx, rw, alpha, K))
+    assert not got[:, ::10].any()
+    # K = 0 companion call: every dot 0, every scaled output 0, every repacked bit -1
+    e = torch.empty(64, 0, dtype=torch.int64, device=DEV)
+    f = torch.empty(1000, 0, dtype=torch.int64, device=DEV)
+    assert not bnn.gemm_u64(e, f, 0).any()
+    assert not bnn.gemm_u64_scaled(e, f, d["alpha"].to(DEV), 0).any()
+
+
+def _sample_pairs(rng, M, N, count):
+    return rng.integers(0, M, count), rng.integers(0, N, count)
+
+
+def test_workload_ffn_4096_sampled():
+    d = workloads.make("ffn_4096")
+    K = d["K"]
+    xp = bnn.pack_signs(d["x"].to(DEV))
+    wp = bnn.pack_signs(d["w"].to(DEV))
+    rx, rw = oracle.pack(workloads.bf16_bits(d["x"])), oracle.pack(d["w"].numpy())
+    assert np.array_equal(words_np(xp), rx) and np.array_equal(words_np(wp), rw)
+    y = bnn.gemm_u64_scaled(xp, wp, d["alpha"].to(DEV), K)   # the benchmark's launch
+    rng = np.random.default_rng(44)
+    mi, ni = _sample_pairs(rng, 4096, 11008, 20000)
+    mi = np.concatenate([mi, [0, 4095, 0, 4095]])
+    ni = np.concatenate([ni, [0, 11007, 11007, 0]])
+    dots = oracle.dot_pairs(rx, rw, K, mi, ni)
+    ref = dots.astype(np.float32) * d["alpha"].numpy()[ni]
+    got = y.cpu().numpy()[mi, ni]
+    assert_scaled_equal(got, ref)
+    # two whole rows, every column
+    rows = np.array([1, 3000])
+    assert_scaled_equal(y.cpu().numpy()[rows],
+                        oracle.gemm_scaled(rx[rows], rw, d["alpha"].numpy(), K))
+
+
+def test_workload_chain_65536():
+    d = workloads.make("chain_65536")
+    dims = d["dims"]
+    x = d["x"]
+    h = bnn.pack_signs(x.to(DEV))
+    wps = [bnn.pack_signs(w.to(DEV)) for w in d["weights"]]
+    h1 = bnn.gemm_sign_repack(h, wps[0], dims[0])
+    h2 = bnn.gemm_sign_repack(h1, wps[1], dims[1])
+    y = bnn.gemm_u64_scaled(h2, wps[2], d["alpha"].to(DEV), dims[2])
+    rng = np.random.default_rng(55)
+    rows = np.sort(rng.choice(x.shape[0], 2048, replace=False))
+    rows[0], rows[-1] = 0, x.shape[0] - 1
+    final, hidden = oracle.chain(x.numpy()[rows], [w.numpy() for w in d["weights"]],
+                                 d["alpha"].numpy())
+    assert np.array_equal(words_np(h)[rows], oracle.pack(x.numpy()[rows]))
+    assert np.array_equal(words_np(h1)[rows], hidden[0])
+    assert np.array_equal(words_np(h2)[rows], hidden[1])
+    assert_scaled_equal(y.cpu().numpy()[rows], final)
+    # property at every row: hidden words have zero pad bits and the right shape
+    assert h1.shape == (x.shape[0], 4) and h2.shape == (x.shape[0], 2)
