@@ -26,4 +26,14 @@ __host__ __device__ inline uint64_t tail_mask(int64_t k) {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// acc + popcount(v) as the single accumulate form of v_bcnt_u32_b32.  Written
+// out so that the compiler cannot reassociate a chain of popcount sums into
+// v_add3_u32 trees (one extra VALU op per two words).  Register-only: no
+// memory operand.
+__device__ __forceinline__ uint32_t popc_acc(uint32_t v, uint32_t acc) {
+  uint32_t r;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(v), "v"(acc));
+  return r;
+}
+
 }  // namespace bnn

@@ -108,10 +108,10 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int c = 0; c < kColsPerLane; ++c) {
           uint32_t a = acc[r][c];
-          a = __builtin_popcount(xv.x ^ wv[c].x) + a;
-          a = __builtin_popcount(xv.y ^ wv[c].y) + a;
-          a = __builtin_popcount(xv.z ^ wv[c].z) + a;
-          a = __builtin_popcount(xv.w ^ wv[c].w) + a;
+          a = popc_acc(xv.x ^ wv[c].x, a);
+          a = popc_acc(xv.y ^ wv[c].y, a);
+          a = popc_acc(xv.z ^ wv[c].z, a);
+          a = popc_acc(xv.w ^ wv[c].w, a);
           acc[r][c] = a;
         }
       }
