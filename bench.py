@@ -6,7 +6,8 @@
 Prints ONE JSON line.  A step is one pass of the hot path over one batch of
 synthetic input, inputs already resident in HBM:
 
-  gemv_4096 (default): pack the bf16 activation row (1 x 4096) and run the
+  gemv_4096 (default): one launch of bnn_gemv_act, which sign-packs the
+      bf16 activation row (1 x 4096) inside the kernel and runs the
       alpha-scaled fp32 binary GEMV against a packed 4096 x 4096 weight
       matrix.  Step i reads weight copy i mod R from a ring of R = 256
       distinct copies (512 MiB, twice the 256 MB Infinity Cache), so every
@@ -43,6 +44,9 @@ HBM_PEAK_GBS = 8000.0
 # (2 v_xor_b32 + 2 v_bcnt_u32_b32).
 VALU_LANE_OPS = 256 * 64 * 2.4e9
 ALU_PEAK_BINARY_OPS = VALU_LANE_OPS / 4 * 128
+# Dense FP4 MFMA peak of MI355X (published): 10.1 PFLOP/s.  The matrix-core
+# kernel encodes +-1 as FP4, so one binary MAC is one FP4 MAC (2 ops).
+MFMA_FP4_PEAK_OPS = 10.1e15
 
 
 def log(*a):
@@ -104,40 +108,32 @@ def gemv_leg(args, steps, warmup):
     g = workloads.generator(2002)
     xring = workloads.normal(g, R, 1, K).to(torch.bfloat16).to(dev)
     xring[0].copy_(d["x"].to(dev))
-    xp = torch.empty((1, kw), dtype=torch.int64, device=dev)
     y = torch.empty((1, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(j):
-        bnn.pack_signs(xring[j], out=xp)
-        bnn.gemm_ex(xp, wring[j], K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
-
-    def gemv_only(j):
-        bnn.gemm_ex(xp, wring[j], K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
+        # one launch: the bf16 row is sign-packed inside the GEMV kernel
+        bnn.gemv_act(xring[j], wring[j], K, bnn.EPI_SCALED, alpha=alpha, out=y)
 
     # eager warmup, then capture R steps (one per ring entry) in a HIP graph
     for i in range(max(warmup, 1)):
         step(i % R)
     torch.cuda.synchronize()
-    graphs = {}
 
-    def graph_of(n, body):
-        key = (n, body.__name__)
-        if key not in graphs:
-            gr = torch.cuda.CUDAGraph()
-            s = torch.cuda.Stream(dev)
-            s.wait_stream(stream)
-            with torch.cuda.stream(s):
-                with torch.cuda.graph(gr, stream=s):
-                    for j in range(n):
-                        body(j % R)
-            torch.cuda.synchronize()
-            graphs[key] = gr
-        return graphs[key]
+    def graph_of(n):
+        gr = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(dev)
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(gr, stream=s):
+                for j in range(n):
+                    step(j % R)
+        torch.cuda.synchronize()
+        return gr
 
     full, rem = divmod(steps, R)
-    g_full = graph_of(R, step) if full else None
-    g_rem = graph_of(rem, step) if rem else None
+    g_full = graph_of(R) if full else None
+    g_rem = graph_of(rem) if rem else None
     for gr in (g_full, g_rem):
         if gr is not None:
             gr.replay()
@@ -151,13 +147,11 @@ def gemv_leg(args, steps, warmup):
 
     ms_total = timed(run_steps, 1, stream)
     ms_step = ms_total / steps
-    # dominant kernel alone: R back-to-back GEMV launches in a graph
-    g_gemv = graph_of(R, gemv_only)
-    g_gemv.replay()
-    reps = max(1, steps // R)
-    ms_gemv = timed(g_gemv.replay, reps, stream) / R
-    bytes_gemv = N * kw * 8 + kw * 8 + N * 4 + N * 4          # Wp + xp + alpha + y
-    bytes_step = bytes_gemv + K * 2 + kw * 8                  # + x bf16 read + xp write
+    # the step is one kernel: its average duration is the step time of
+    # back-to-back graph launches (an upper bound: it includes launch gaps)
+    ms_gemv = ms_step
+    bytes_gemv = N * kw * 8 + K * 2 + N * 4 + N * 4           # Wp + x bf16 + alpha + y
+    bytes_step = bytes_gemv
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
     gops = 2.0 * N * K / (ms_step * 1e-3) / 1e9
     achieved = bytes_gemv / (ms_gemv * 1e-3) / 1e9
@@ -169,7 +163,8 @@ def gemv_leg(args, steps, warmup):
                 "bytes_per_step": bytes_step, "hip_graph": True},
         roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                  "kernel": "gemv_kernel (alpha-scaled)", "kernel_avg_us": ms_gemv * 1e3,
+                  "kernel": "gemv_kernel (bf16 activations packed in-kernel, alpha-scaled)",
+                  "kernel_avg_us": ms_gemv * 1e3,
                   "algorithmic_bytes_per_launch": bytes_gemv},
         step_inputs=(d, N, K),
     )
@@ -194,23 +189,28 @@ def ffn_leg(steps, warmup):
         bnn.pack_signs(x, out=xp)
         bnn.gemm_ex(xp, wp, K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
 
-    def gemm_only():
-        bnn.gemm_ex(xp, wp, K, bnn.EPI_SCALED, bnn.ALGO_AUTO, alpha=alpha, out=y)
+    def gemm(algo):
+        return lambda: bnn.gemm_ex(xp, wp, K, bnn.EPI_SCALED, algo, alpha=alpha, out=y)
 
     for _ in range(max(warmup, 1)):
         step()
     ms_step = timed(step, steps, stream)
-    ms_gemm = timed(gemm_only, steps, stream)
+    ms_gemm = timed(gemm(bnn.ALGO_MFMA), steps, stream)       # what AUTO runs at this shape
+    ms_valu = timed(gemm(bnn.ALGO_TILED), max(2, steps // 4), stream)  # the popcount ablation
     ops = 2.0 * M * N * K
+    ach = ops / (ms_gemm * 1e-3)
     return dict(
         value=ops / (ms_step * 1e-3) / 1e9, unit="binary GOPS", ms_per_step=ms_step,
         config={"workload": "ffn_4096", "M": M, "K": K, "N": N, "x_dtype": "bf16",
                 "w_dtype": "fp32 (packed offline)", "epilogue": "alpha-scaled fp32"},
-        roofline={"bound": "alu", "achieved": ops / (ms_gemm * 1e-3) / 1e12,
-                  "peak": ALU_PEAK_BINARY_OPS / 1e12, "unit": "T binary-ops/s",
-                  "frac": ops / (ms_gemm * 1e-3) / ALU_PEAK_BINARY_OPS, "traffic": None,
-                  "kernel": "gemm_tiled_kernel (alpha-scaled)", "kernel_avg_us": ms_gemm * 1e3,
-                  "algorithmic_ops_per_launch": ops},
+        roofline={"bound": "mfma", "achieved": ach / 1e12, "peak": MFMA_FP4_PEAK_OPS / 1e12,
+                  "unit": "T binary-ops/s (= FP4 TFLOP/s)", "frac": ach / MFMA_FP4_PEAK_OPS,
+                  "traffic": None, "kernel": "gemm_mfma_kernel (alpha-scaled)",
+                  "kernel_avg_us": ms_gemm * 1e3, "algorithmic_ops_per_launch": ops,
+                  "frac_of_valu_popcount_peak": ach / ALU_PEAK_BINARY_OPS},
+        ablation={"valu_xor_popcount_us": ms_valu * 1e3, "mfma_fp4_us": ms_gemm * 1e3,
+                  "valu_xor_popcount_frac_of_valu_peak": ops / (ms_valu * 1e-3) / ALU_PEAK_BINARY_OPS,
+                  "speedup_mfma_over_valu": ms_valu / ms_gemm},
         step_inputs=(d, N, K),
     )
 
@@ -251,10 +251,10 @@ def chain_leg(steps, warmup):
         value=ops / (ms_step * 1e-3) / 1e9, unit="binary GOPS", ms_per_step=ms_step,
         config={"workload": "chain_65536", "M": M, "dims": list(dims), "x_dtype": "fp32",
                 "hidden": "sign->repack u64", "epilogue": "alpha-scaled fp32"},
-        roofline={"bound": "alu", "achieved": ops1 / (ms_l1 * 1e-3) / 1e12,
-                  "peak": ALU_PEAK_BINARY_OPS / 1e12, "unit": "T binary-ops/s",
-                  "frac": ops1 / (ms_l1 * 1e-3) / ALU_PEAK_BINARY_OPS, "traffic": None,
-                  "kernel": "gemm_tiled_kernel (sign->repack, layer 1)",
+        roofline={"bound": "mfma", "achieved": ops1 / (ms_l1 * 1e-3) / 1e12,
+                  "peak": MFMA_FP4_PEAK_OPS / 1e12, "unit": "T binary-ops/s (= FP4 TFLOP/s)",
+                  "frac": ops1 / (ms_l1 * 1e-3) / MFMA_FP4_PEAK_OPS, "traffic": None,
+                  "kernel": "gemm_mfma_kernel (sign->repack, layer 1)",
                   "kernel_avg_us": ms_l1 * 1e3, "algorithmic_ops_per_launch": ops1},
         step_inputs=(d, None, None),
     )
@@ -274,7 +274,7 @@ def cpu_baseline(workload, step_inputs, seconds):
         alpha = d["alpha"].numpy()
         xb = workloads.bf16_bits(d["x"])
         kw = oracle.words(K)
-        bytes_step = N * kw * 8 + kw * 8 + N * 8 + K * 2 + kw * 8
+        bytes_step = N * kw * 8 + K * 2 + N * 8   # as the GPU step: Wp + x bf16 + alpha + y
         n, t0 = 0, time.perf_counter()
         while True:
             xp = oracle.pack(xb)
@@ -358,11 +358,14 @@ def main():
     }
     if "binary_gops" in res:
         out["binary_gops"] = res["binary_gops"]
+    if "ablation" in res:
+        out["ablation"] = res["ablation"]
     if args.workload == "gemv_4096" and not args.no_secondary and not args.rows:
         sec = ffn_leg(10, 2)
         log(f"[bench] secondary ffn_4096: {sec['value']:.1f} binary GOPS")
         out["secondary"] = {"workload": "ffn_4096", "value": sec["value"], "unit": sec["unit"],
-                            "ms_per_step": sec["ms_per_step"], "roofline": sec["roofline"]}
+                            "ms_per_step": sec["ms_per_step"], "roofline": sec["roofline"],
+                            "ablation": sec["ablation"]}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(args.workload, res["step_inputs"], args.cpu_seconds)

@@ -47,7 +47,8 @@
  * on error nothing is written or launched and a non-zero bnn_status is
  * returned.  A pointer may be NULL only when the buffer it names has no
  * elements.  M = 0 or N = 0 returns BNN_OK without a launch.  K = 0 is valid
- * and launches (dots are 0).  Dimensions must be >= 0 and < 2^31.  A launch
+ * and launches (dots are 0).  Dimensions (M, N, K, rows, leading
+ * dimensions) must be >= 0 and < 2^30, else BNN_E_SHAPE.  A launch
  * failure reported by the HIP runtime right after the launch returns
  * BNN_E_LAUNCH; faults during execution surface at the caller's next
  * synchronization, as for any HIP kernel.
@@ -88,9 +89,12 @@ typedef enum bnn_epilogue {
 
 /* Kernel family (see bnn_gemm_ex).  AUTO picks by shape. */
 typedef enum bnn_algo {
-  BNN_ALGO_AUTO = 0,  /* GEMV for small M, tiled GEMM otherwise */
+  BNN_ALGO_AUTO = 0,  /* GEMV for M <= 8; MFMA for larger M while K <= 2^24;
+                         TILED beyond */
   BNN_ALGO_GEMV = 1,  /* weight-streaming kernel; any M, fastest at M <= 8 */
-  BNN_ALGO_TILED = 2  /* LDS-tiled XOR + popcount GEMM */
+  BNN_ALGO_TILED = 2, /* LDS-tiled VALU XOR + popcount GEMM; any K */
+  BNN_ALGO_MFMA = 3   /* matrix-core GEMM: +-1 as FP4 operands, exact fp32
+                         accumulation; K <= 2^24 (else BNN_E_SHAPE) */
 } bnn_algo;
 
 /* ceil(k / 64): 64-bit words per packed row of k logical values; 0 for
@@ -170,7 +174,9 @@ bnn_status bnn_gemm_sign_repack(const uint64_t *xp, const uint64_t *wp, uint64_t
 
 /*
  * bnn_gemm_ex -- the general form of the three products above, with an
- * explicit kernel family.  `y` is int32*, float* or uint64* according to
+ * explicit kernel family (see bnn_algo; the matrix-core family takes the
+ * same exact integer sum of +-1 products on the MFMA units, which "Binary
+ * Math Effectiveness", section 3, names as the faster dense unit).  `y` is int32*, float* or uint64* according to
  * `epilogue` (BNN_EPI_*); `alpha` is read only for BNN_EPI_SCALED.  `algo`
  * is a BNN_ALGO_* value; every family gives bit-identical results, so the
  * selector only changes speed.  Errors as above, plus BNN_E_ARG for an
@@ -178,6 +184,28 @@ bnn_status bnn_gemm_sign_repack(const uint64_t *xp, const uint64_t *wp, uint64_t
  */
 bnn_status bnn_gemm_ex(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
                        int64_t M, int64_t N, int64_t K, int epilogue, int algo, void *stream);
+
+/*
+ * bnn_gemv_act -- the weight-streaming product for small M with the
+ * activation packing fused in: x holds M real-valued rows (fp32 or bf16,
+ * row stride ldx elements, ldx >= K), which the kernel sign-projects and
+ * packs exactly as bnn_pack_signs would before taking the product with the
+ * packed weights wp.  The result equals bnn_pack_signs followed by
+ * bnn_gemm_ex with the same epilogue, bit for bit.  ("Binary Math
+ * Effectiveness", section 1, for the projection and the identity;
+ * sections 2.2-2.3 for the batch-1 regime it serves: one launch per
+ * decode step, weights streamed once.)
+ *
+ *   x         M x ldx values of type `dtype`, element-aligned.
+ *   wp        N x bnn_words(K) packed weights, 8-byte aligned.
+ *   alpha, y  as for bnn_gemm_ex with `epilogue`.
+ * Intended for M <= 8; larger M is correct but streams W once per 8 rows
+ * (pack once with bnn_pack_signs and use bnn_gemm_ex instead).  Errors as
+ * bnn_gemm_ex, plus BNN_E_DTYPE, and BNN_E_SHAPE when ldx < K.
+ */
+bnn_status bnn_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
+                        const float *alpha, void *y, int64_t M, int64_t N, int64_t K, int epilogue,
+                        void *stream);
 
 #ifdef __cplusplus
 }

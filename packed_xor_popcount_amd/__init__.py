@@ -25,8 +25,9 @@ import torch
 
 __all__ = [
     "BnnError", "EPI_I32", "EPI_SCALED", "EPI_REPACK", "ALGO_AUTO", "ALGO_GEMV", "ALGO_TILED",
+    "ALGO_MFMA",
     "library", "library_path", "words", "pack_signs", "gemm_u64", "gemm_u64_scaled",
-    "gemm_sign_repack", "gemm_ex", "version",
+    "gemm_sign_repack", "gemm_ex", "gemv_act", "version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,10 +35,10 @@ library_path = os.path.join(_HERE, "libbnn.so")
 
 BNN_FP32, BNN_BF16 = 0, 1
 EPI_I32, EPI_SCALED, EPI_REPACK = 0, 1, 2
-ALGO_AUTO, ALGO_GEMV, ALGO_TILED = 0, 1, 2
+ALGO_AUTO, ALGO_GEMV, ALGO_TILED, ALGO_MFMA = 0, 1, 2, 3
 
 EXPORTED = ("bnn_words", "bnn_status_str", "bnn_version", "bnn_pack_signs", "bnn_gemm_u64",
-            "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex")
+            "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex", "bnn_gemv_act")
 
 
 class BnnError(RuntimeError):
@@ -69,8 +70,9 @@ def library():
     lib.bnn_gemm_u64_scaled.argtypes = [P, P, P, P, I64, I64, I64, P]
     lib.bnn_gemm_sign_repack.argtypes = [P, P, P, I64, I64, I64, P]
     lib.bnn_gemm_ex.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
+    lib.bnn_gemv_act.argtypes = [P, I, I64, P, P, P, I64, I64, I64, I, P]
     for name in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack",
-                 "bnn_gemm_ex"):
+                 "bnn_gemm_ex", "bnn_gemv_act"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -146,7 +148,7 @@ def gemm_ex(xp: torch.Tensor, wp: torch.Tensor, K: int, epilogue: int = EPI_I32,
             out: torch.Tensor | None = None):
     """General packed product (bnn_gemm_ex): int32 (EPI_I32), alpha-scaled
     fp32 (EPI_SCALED) or packed signs (EPI_REPACK), with an explicit kernel
-    family (ALGO_AUTO, ALGO_GEMV, ALGO_TILED)."""
+    family (ALGO_AUTO, ALGO_GEMV, ALGO_TILED, ALGO_MFMA)."""
     M = _packed("xp", xp, K)
     N = _packed("wp", wp, K)
     if wp.device != xp.device:
@@ -155,6 +157,14 @@ def gemm_ex(xp: torch.Tensor, wp: torch.Tensor, K: int, epilogue: int = EPI_I32,
         _need_cuda("alpha", alpha)
         if alpha.dtype != torch.float32 or alpha.shape != (N,) or not alpha.is_contiguous():
             raise ValueError("alpha must be a contiguous float32 tensor of shape (N,)")
+    out = _out_for(epilogue, M, N, xp.device, out)
+    st = library().bnn_gemm_ex(_ptr(xp), _ptr(wp), _ptr(alpha) if epilogue == EPI_SCALED else None,
+                               _ptr(out), M, N, int(K), int(epilogue), int(algo), _stream(xp))
+    _check(st, "bnn_gemm_ex")
+    return out
+
+
+def _out_for(epilogue: int, M: int, N: int, device, out):
     if epilogue == EPI_I32:
         shape, dtype = (M, N), torch.int32
     elif epilogue == EPI_SCALED:
@@ -164,12 +174,40 @@ def gemm_ex(xp: torch.Tensor, wp: torch.Tensor, K: int, epilogue: int = EPI_I32,
     else:
         raise ValueError(f"unknown epilogue {epilogue}")
     if out is None:
-        out = torch.empty(shape, dtype=dtype, device=xp.device)
-    elif tuple(out.shape) != shape or out.dtype != dtype or not out.is_contiguous():
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(out.shape) != shape or out.dtype != dtype or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous {dtype} tensor of shape {shape}")
-    st = library().bnn_gemm_ex(_ptr(xp), _ptr(wp), _ptr(alpha) if epilogue == EPI_SCALED else None,
-                               _ptr(out), M, N, int(K), int(epilogue), int(algo), _stream(xp))
-    _check(st, "bnn_gemm_ex")
+    return out
+
+
+def gemv_act(x: torch.Tensor, wp: torch.Tensor, K: int | None = None, epilogue: int = EPI_I32,
+             alpha: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """Product of real-valued activation rows ``x`` (fp32 or bf16, 2-D, unit
+    stride along the last dimension; the first ``K`` columns are used) with
+    packed weights ``wp``; the kernel packs ``x`` itself (bnn_gemv_act).
+    Meant for small M (batch-1 decode)."""
+    _need_cuda("x", x)
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit stride along its last dimension")
+    if x.dtype == torch.float32:
+        dt = BNN_FP32
+    elif x.dtype == torch.bfloat16:
+        dt = BNN_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    M, cols = x.shape
+    K = cols if K is None else int(K)
+    N = _packed("wp", wp, K)
+    if epilogue == EPI_SCALED:
+        _need_cuda("alpha", alpha)
+        if alpha.dtype != torch.float32 or alpha.shape != (N,) or not alpha.is_contiguous():
+            raise ValueError("alpha must be a contiguous float32 tensor of shape (N,)")
+    out = _out_for(epilogue, M, N, x.device, out)
+    ldx = x.stride(0) if M > 1 else max(cols, 1)
+    st = library().bnn_gemv_act(_ptr(x), dt, ldx, _ptr(wp),
+                                _ptr(alpha) if epilogue == EPI_SCALED else None, _ptr(out),
+                                M, N, K, int(epilogue), _stream(x))
+    _check(st, "bnn_gemv_act")
     return out
 
 

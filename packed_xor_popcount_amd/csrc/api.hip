@@ -17,8 +17,9 @@ bnn_status launch_status(hipError_t e) { return e == hipSuccess ? BNN_OK : BNN_E
 bnn_status check_gemm(const uint64_t *xp, const uint64_t *wp, const float *alpha, const void *y,
                       int64_t M, int64_t N, int64_t K, int epilogue, int algo) {
   if (epilogue < BNN_EPI_I32 || epilogue > BNN_EPI_REPACK) return BNN_E_ARG;
-  if (algo < BNN_ALGO_AUTO || algo > BNN_ALGO_TILED) return BNN_E_ARG;
+  if (algo < BNN_ALGO_AUTO || algo > BNN_ALGO_MFMA) return BNN_E_ARG;
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return BNN_E_SHAPE;
+  if (algo == BNN_ALGO_MFMA && K > bnn::kMfmaMaxK) return BNN_E_SHAPE;
   const int64_t kw = bnn_words(K);
   if ((M * kw > 0 && !xp) || (N * kw > 0 && !wp) || (M * N > 0 && !y)) return BNN_E_NULL;
   if (epilogue == BNN_EPI_SCALED && M * N > 0 && !alpha) return BNN_E_NULL;
@@ -67,9 +68,38 @@ bnn_status bnn_gemm_ex(const uint64_t *xp, const uint64_t *wp, const float *alph
   if (st != BNN_OK) return st;
   if (M == 0 || N == 0) return BNN_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool gemv = algo == BNN_ALGO_GEMV || (algo == BNN_ALGO_AUTO && M <= kGemvMaxM);
-  if (gemv) return launch_status(bnn::launch_gemv(xp, wp, alpha, y, M, N, K, epilogue, s));
+  if (algo == BNN_ALGO_AUTO) {
+    if (M <= kGemvMaxM)
+      algo = BNN_ALGO_GEMV;  // weight-streaming: HBM-bound
+    else if (K <= bnn::kMfmaMaxK)
+      algo = BNN_ALGO_MFMA;  // matrix cores: ~8x the VALU popcount rate
+    else
+      algo = BNN_ALGO_TILED;
+  }
+  if (algo == BNN_ALGO_GEMV)
+    return launch_status(bnn::launch_gemv(xp, wp, alpha, y, M, N, K, epilogue, s));
+  if (algo == BNN_ALGO_MFMA)
+    return launch_status(bnn::launch_gemm_mfma(xp, wp, alpha, y, M, N, K, epilogue, s));
   return launch_status(bnn::launch_gemm_tiled(xp, wp, alpha, y, M, N, K, epilogue, s));
+}
+
+bnn_status bnn_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
+                        const float *alpha, void *y, int64_t M, int64_t N, int64_t K, int epilogue,
+                        void *stream) {
+  if (dtype != BNN_FP32 && dtype != BNN_BF16) return BNN_E_DTYPE;
+  if (epilogue < BNN_EPI_I32 || epilogue > BNN_EPI_REPACK) return BNN_E_ARG;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || ldx < K ||
+      ldx >= kMaxDim)
+    return BNN_E_SHAPE;
+  const int64_t kw = bnn_words(K);
+  if ((M * K > 0 && !x) || (N * kw > 0 && !wp) || (M * N > 0 && !y)) return BNN_E_NULL;
+  if (epilogue == BNN_EPI_SCALED && M * N > 0 && !alpha) return BNN_E_NULL;
+  if (misaligned(x, dtype == BNN_FP32 ? 4 : 2) || misaligned(wp, 8)) return BNN_E_ALIGN;
+  if (misaligned(y, epilogue == BNN_EPI_REPACK ? 8 : 4)) return BNN_E_ALIGN;
+  if (epilogue == BNN_EPI_SCALED && misaligned(alpha, 4)) return BNN_E_ALIGN;
+  if (M == 0 || N == 0) return BNN_OK;
+  return launch_status(bnn::launch_gemv_act(x, dtype, ldx, wp, alpha, y, M, N, K, epilogue,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 bnn_status bnn_gemm_u64(const uint64_t *xp, const uint64_t *wp, int32_t *y, int64_t M, int64_t N,

@@ -15,8 +15,18 @@ hipError_t launch_pack(const void *src, int dtype, int64_t rows, int64_t k, int6
 hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
                              int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
 
+// Matrix-core (FP4 MFMA) GEMM; exact while K <= 2^24.
+hipError_t launch_gemm_mfma(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+                            int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
+
 hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
                        int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
+
+// GEMV whose activation rows arrive as fp32 (dtype 0) or bf16 (dtype 1)
+// values, row stride ldx elements, and are sign-packed inside the kernel.
+hipError_t launch_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
+                           const float *alpha, void *y, int64_t M, int64_t N, int64_t K,
+                           int epilogue, hipStream_t s);
 
 // Mask of the logical bits of a row's last 64-bit word.
 __host__ __device__ inline uint64_t tail_mask(int64_t k) {
@@ -25,6 +35,7 @@ __host__ __device__ inline uint64_t tail_mask(int64_t k) {
 }
 
 constexpr int kWave = 64;  // CDNA wavefront width
+constexpr int64_t kMfmaMaxK = int64_t(1) << 24;  // fp32 accumulation of +-1 is exact up to here
 
 // acc + popcount(v) as the single accumulate form of v_bcnt_u32_b32.  Written
 // out so that the compiler cannot reassociate a chain of popcount sums into

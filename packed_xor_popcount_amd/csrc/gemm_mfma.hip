@@ -1,0 +1,323 @@
+// gemm_mfma.hip -- packed binary GEMM on the gfx950 matrix cores (large M).
+//
+// The result is the same integer as the XOR + popcount kernels:
+// <x_m, w_n> = K - 2 * popcount(x_m XOR w_n) = sum_k x[k] * w[k] over the K
+// logical elements, x, w in {+1, -1} ("Binary Math Effectiveness -- why /
+// how / when", section 1: the identity is exact, so the plain sum of
+// products is the same number).  Section 3 of that page notes that dense
+// tensor units usually beat naive bit kernels; on MI355X the FP4 matrix
+// rate is about 8x the VALU XOR + popcount issue rate, so for large M the
+// sum of products is taken on the matrix cores instead:
+//
+//  * a packed bit b is an FP4 (e2m1) operand value (+1.0 = 0x2 when b = 0,
+//    -1.0 = 0xA when b = 1): the packed bit IS the FP4 sign bit, so no table
+//    is needed.  A 32-bit chunk x of a packed row becomes the four operand
+//    registers ((x << (3 - r)) & 0x88888888) | 0x22222222, r = 0..3, i.e.
+//    register r nibble j holds bit 4j + r.  This permutes the K elements
+//    inside the chunk; a dot product does not depend on the order of its
+//    terms, and A and B are unpacked by the same rule, so the product is
+//    unchanged.  Seven VALU ops unpack 32 elements.
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 with both operands FP4 and unit
+//    scales (E8M0 127) accumulates in fp32.  Each product is +-1 (or 0 for a
+//    masked pad element), so every partial sum is an integer of magnitude
+//    <= K and is exact while K <= 2^24 (the library uses this kernel only
+//    then).  The final fp32 accumulator IS the integer dot.
+//  * pad elements (k >= K) get zero nibbles in the A operand, so they add
+//    nothing whatever the pad bits of either operand hold.
+//
+// Tiling: block = 4 waves arranged WR x WC; a wave owns RB x CB tiles of
+// 32 x 32 outputs.  Per step of 8 words (512 elements of K) each lane loads
+// its rows' / columns' words straight from L2 (lanes 0-31: words k0..k0+3;
+// lanes 32-63: words k0+4..k0+7; the eight MFMA slices pair the low or high
+// halves of those words), unpacks them in registers and issues RB*CB*8
+// MFMAs; the next step's words are loaded before the current step's MFMAs.
+// Output layout of a 32 x 32 tile (lane l, accumulator register v): column
+// l % 32, row 8 (v / 4) + 4 (l / 32) + v % 4.  The repack epilogue ballots
+// two neighbouring tiles: the low 32 ballot bits are one row's 32 columns,
+// the high 32 bits those of the row 4 below.
+#include "../../include/bnn.h"
+#include "bnn_internal.h"
+
+namespace bnn {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Wave arrangement and per-wave tiles of the wide-output configuration.
+#ifndef BNN_MFMA_WR
+#define BNN_MFMA_WR 4
+#define BNN_MFMA_WC 1
+#define BNN_MFMA_RB 2
+#define BNN_MFMA_CB 2
+#endif
+
+constexpr int kScaleOne = 0x7F7F7F7F;  // E8M0 127 = 2^0 in every byte
+constexpr int kFmtFp4 = 4;             // cbsz / blgp: e2m1
+
+// (a & m) | c as one v_and_or_b32.  gfx9 VOP3 encodings take no literal, so
+// the compiler would otherwise emit v_and + v_or with literals; with m and c
+// held in VGPRs (hoisted out of every loop) it is one op.  Register-only.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
+// Operands of both 32-element halves of a packed word w: register r of the
+// half's operand is ((half << (3 - r)) & 0x88888888) | 0x22222222.  One
+// 64-bit shift serves both halves: the bits it carries from the low half
+// into the high half land in bit positions 0..2, which the mask drops.
+// Eleven VALU ops for 64 elements.
+__device__ __forceinline__ void fp4_operands(uint64_t w, uint32_t c8, uint32_t c2, v8i &lo,
+                                             v8i &hi) {
+  const uint64_t s1 = w << 1, s2 = w << 2, s3 = w << 3;
+  lo[0] = (int)and_or((uint32_t)s3, c8, c2);
+  lo[1] = (int)and_or((uint32_t)s2, c8, c2);
+  lo[2] = (int)and_or((uint32_t)s1, c8, c2);
+  lo[3] = (int)and_or((uint32_t)w, c8, c2);
+  hi[0] = (int)and_or((uint32_t)(s3 >> 32), c8, c2);
+  hi[1] = (int)and_or((uint32_t)(s2 >> 32), c8, c2);
+  hi[2] = (int)and_or((uint32_t)(s1 >> 32), c8, c2);
+  hi[3] = (int)and_or((uint32_t)(w >> 32), c8, c2);
+  lo[4] = lo[5] = lo[6] = lo[7] = 0;
+  hi[4] = hi[5] = hi[6] = hi[7] = 0;
+}
+
+// Zero the nibbles of elements whose bit in `valid` is 0 (same permutation
+// as fp4_operand).
+__device__ __forceinline__ v8i mask_operand(v8i a, uint32_t valid) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t s = (valid << (3 - r)) & 0x88888888u;
+    const uint32_t fill = s | (s >> 1) | (s >> 2) | (s >> 3);
+    a[r] = (int)((uint32_t)a[r] & fill);
+  }
+  return a;
+}
+
+__device__ __forceinline__ uint32_t valid_bits(int64_t e, int64_t K) {
+  if (e >= K) return 0u;
+  const int64_t left = K - e;
+  return left >= 32 ? 0xFFFFFFFFu : ((1u << left) - 1u);
+}
+
+template <int EPI, int WR, int WC, int RB, int CB>
+__global__ void __launch_bounds__(256)
+    gemm_mfma_kernel(const uint64_t *__restrict__ xp, const uint64_t *__restrict__ wp,
+                     const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
+                     int kw, int tiles_n) {
+  static_assert(WR * WC == 4, "4 waves per block");
+  static_assert(EPI != BNN_EPI_REPACK || CB % 2 == 0, "repack pairs 32-column tiles");
+  constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - (blockIdx.x / tiles_n) * tiles_n;
+  const int m0 = tm * BM + (wave / WC) * (RB * 32);
+  const int n0 = tn * BN + (wave % WC) * (CB * 32);
+  const int h = lane >> 5;    // which word pair of a 4-word step
+  const int li = lane & 31;   // row / column within a 32 x 32 tile
+
+  // Row / column pointers, clamped into the matrices (rows past M and
+  // columns past N compute garbage that is never stored).
+  const uint64_t *arow[RB];
+  const uint64_t *bcol[CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int m = m0 + rb * 32 + li;
+    m = m < M ? m : M - 1;
+    arow[rb] = xp + (int64_t)m * kw;
+  }
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    int n = n0 + cb * 32 + li;
+    n = n < N ? n : N - 1;
+    bcol[cb] = wp + (int64_t)n * kw;
+  }
+
+  float a_pre[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int n = n0 + cb * 32 + li;
+    a_pre[cb] = (EPI == BNN_EPI_SCALED && n < N) ? alpha[n] : 0.0f;
+  }
+  v16f acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+
+  // Steps of kSW = 8 words (512 elements of K): lanes 0-31 hold words
+  // k0 .. k0+3 of their row / column, lanes 32-63 words k0+4 .. k0+7; slice
+  // q (0..7) pairs half (q & 1) of word (q >> 1) of both lane halves.  A step
+  // is "clean" when all its elements are inside K; only the last step can
+  // be partial.
+  constexpr int kSW = 8, kHW = kSW / 2;
+  const int nsteps = (kw + kSW - 1) / kSW;
+  const int nclean = (K >> 6) / kSW;
+
+  const uint32_t c8 = 0x88888888u, c2 = 0x22222222u;
+  typedef uint64_t ABuf[RB][kHW];
+  typedef uint64_t BBuf[CB][kHW];
+  auto load_clean = [&](int s, ABuf &a, BBuf &b) {
+    const int w = s * kSW + kHW * h;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < kHW; ++i) a[rb][i] = arow[rb][w + i];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < kHW; ++i) b[cb][i] = bcol[cb][w + i];
+  };
+  auto mma_step = [&](const ABuf &a, const BBuf &b, bool masked, int s) {
+    // word i of this lane's half feeds slices 2i (low 32) and 2i+1 (high 32)
+#pragma unroll
+    for (int i = 0; i < kHW; ++i) {
+      v8i ao[2][RB], bo[2][CB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) fp4_operands(a[rb][i], c8, c2, ao[0][rb], ao[1][rb]);
+      if (masked) {
+        const int64_t e = (int64_t)(s * kSW + kHW * h + i) * 64;
+        const uint32_t v0 = valid_bits(e, K), v1 = valid_bits(e + 32, K);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          ao[0][rb] = mask_operand(ao[0][rb], v0);
+          ao[1][rb] = mask_operand(ao[1][rb], v1);
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) fp4_operands(b[cb][i], c8, c2, bo[0][cb], bo[1][cb]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ao[q][rb], bo[q][cb], acc[rb][cb], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
+    }
+  };
+
+  // Two register buffers in ping-pong: the loads of step s+1 are in flight
+  // while step s runs.  Both halves of the pair loop are unconditional (a
+  // conditional use would let the compiler sink the prefetch behind the
+  // MFMAs); the load past the last clean step re-reads that step (clamped,
+  // in bounds, unused).  An odd last step runs after the loop.
+  ABuf a0, a1;
+  BBuf b0, b1;
+  if (nclean > 0) load_clean(0, a0, b0);
+  int s = 0;
+  for (; s + 1 < nclean; s += 2) {
+    load_clean(s + 1, a1, b1);
+    mma_step(a0, b0, false, s);
+    load_clean(s + 2 < nclean ? s + 2 : nclean - 1, a0, b0);
+    mma_step(a1, b1, false, s + 1);
+  }
+  if (s < nclean) mma_step(a0, b0, false, s);
+  if (nclean < nsteps) {  // the partial last step: guarded loads, masked A
+    const int w = nclean * kSW + kHW * h;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < kHW; ++i) a0[rb][i] = w + i < kw ? arow[rb][w + i] : 0;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int i = 0; i < kHW; ++i) b0[cb][i] = w + i < kw ? bcol[cb][w + i] : 0;
+    mma_step(a0, b0, true, nclean);
+  }
+
+  // Epilogue.  acc[rb][cb][v] is the exact integer dot of row
+  // m0 + rb*32 + 8(v/4) + 4h + v%4 and column n0 + cb*32 + li.
+  if (EPI == BNN_EPI_REPACK) {
+    const int nw = (N + 63) >> 6;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cp = 0; cp < CB / 2; ++cp) {
+        const int na = n0 + (2 * cp) * 32 + li, nb2 = na + 32;
+        const int wi = (n0 >> 6) + cp;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint64_t lo = __builtin_amdgcn_ballot_w64(na < N && acc[rb][2 * cp][v] <= 0.0f);
+          const uint64_t hi = __builtin_amdgcn_ballot_w64(nb2 < N && acc[rb][2 * cp + 1][v] <= 0.0f);
+          const int r0 = m0 + rb * 32 + 8 * (v >> 2) + (v & 3);
+          // lane 0 writes row r0, lane 32 writes row r0 + 4
+          const int r = r0 + 4 * h;
+          const uint64_t word = h ? ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32))
+                                  : ((hi << 32) | (lo & 0xFFFFFFFFull));
+          if (li == 0 && r < M && wi < nw) static_cast<uint64_t *>(yv)[(int64_t)r * nw + wi] = word;
+        }
+      }
+  } else {
+    // Row r(v) = 8 (v / 4) + v % 4 of a 32-row tile (plus 4h): four row
+    // pointers, stepped by 8 rows.  Tiles wholly inside M skip the row test.
+    const int64_t ld = N;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int mt = m0 + rb * 32 + 4 * h;  // row of v = 0 for this lane
+      const bool full_rows = m0 + rb * 32 + 32 <= M;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int n = n0 + cb * 32 + li;
+        if (n >= N) continue;
+        const float a = a_pre[cb];
+        if (EPI == BNN_EPI_I32) {
+          int32_t *p = static_cast<int32_t *>(yv) + (int64_t)mt * ld + n;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int dr = 8 * (v >> 2) + (v & 3);
+            if (full_rows || mt + dr < M) p[dr * ld] = (int)acc[rb][cb][v];
+          }
+        } else {
+          float *p = static_cast<float *>(yv) + (int64_t)mt * ld + n;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int dr = 8 * (v >> 2) + (v & 3);
+            if (full_rows || mt + dr < M) p[dr * ld] = __fmul_rn(acc[rb][cb][v], a);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int EPI, int WR, int WC, int RB, int CB>
+hipError_t launch_cfg(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
+                      int N, int K, hipStream_t s) {
+  constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
+  const int kw = (K + 63) / 64;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * tiles_n;
+  hipLaunchKernelGGL((gemm_mfma_kernel<EPI, WR, WC, RB, CB>), dim3((unsigned)tiles), dim3(256), 0,
+                     s, xp, wp, alpha, y, M, N, K, kw, tiles_n);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
+                      int N, int K, hipStream_t s) {
+  // Narrow outputs stack the four waves along M so that no wave idles.
+  if (N <= 64) return launch_cfg<EPI, 4, 1, 1, 2>(xp, wp, alpha, y, M, N, K, s);  // 128 x 64
+  return launch_cfg<EPI, BNN_MFMA_WR, BNN_MFMA_WC, BNN_MFMA_RB, BNN_MFMA_CB>(xp, wp, alpha, y, M, N,
+                                                                          K, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mfma(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+                            int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s) {
+  switch (epilogue) {
+    case BNN_EPI_I32:
+      return launch_epi<BNN_EPI_I32>(xp, wp, alpha, y, (int)M, (int)N, (int)K, s);
+    case BNN_EPI_SCALED:
+      return launch_epi<BNN_EPI_SCALED>(xp, wp, alpha, y, (int)M, (int)N, (int)K, s);
+    default:
+      return launch_epi<BNN_EPI_REPACK>(xp, wp, alpha, y, (int)M, (int)N, (int)K, s);
+  }
+}
+
+}  // namespace bnn

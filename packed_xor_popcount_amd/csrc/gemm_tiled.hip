@@ -60,6 +60,16 @@ __global__ void __launch_bounds__(256)
   const int n0 = tn * kBN;
   const uint64_t tmask = tail_mask(K);
 
+  // Scales of this lane's columns, fetched before the K loop (on gfx9 the
+  // vector-memory counter also counts stores, so a load between the
+  // epilogue's stores would make later waits drain them).
+  float a_pre[kColsPerLane];
+#pragma unroll
+  for (int c = 0; c < kColsPerLane; ++c) {
+    const int n = n0 + lane + 64 * c;
+    a_pre[c] = (EPI == BNN_EPI_SCALED && n < N) ? alpha[n] : 0.0f;
+  }
+
   uint32_t acc[kRowsPerWave][kColsPerLane];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r)
@@ -123,8 +133,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int c = 0; c < kColsPerLane; ++c) {
     const int n = n0 + lane + 64 * c;
-    float a = 0.0f;
-    if (EPI == BNN_EPI_SCALED && n < N) a = alpha[n];
+    const float a = a_pre[c];
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       const int m = m0 + r;

@@ -1,5 +1,5 @@
 // gemv.hip -- weight-streaming XOR + popcount product for small M (batch-1
-// decode and similar).
+// decode and similar), with an optional fused activation packer.
 //
 // Same result as the tiled GEMM: <x_m, w_n> = K - 2 * popcount(x_m XOR w_n)
 // over the K logical bits ("Binary Math Effectiveness -- why / how / when",
@@ -10,162 +10,292 @@
 // Design for gfx950 (HBM-bound):
 //  * L lanes (a power of two, 4..64) share one column n = one row of W;
 //    each lane reads VEC consecutive words (16 B when VEC = 2) per step, so a
-//    wave reads G = 64/L whole W rows with fully coalesced loads.
-//  * block = 4 wavefronts; one block step covers 4 * G * P columns, the
-//    loads of all P passes issued before any popcount; up to 8 activation
-//    rows share every W word loaded (rows beyond 8 re-stream W).
+//    wave reads G = 64/L whole W rows with fully coalesced loads, and the
+//    next step's W words are loaded before the current step's popcounts.
+//  * block = 4 wavefronts; one block step covers CB = 4 * G * P columns
+//    (P = 1 for latency-bound sizes, 4 when streaming large W, 64 / (4G)
+//    for repack); a persistent grid of at most 8 blocks per CU strides over
+//    the steps.  Up to 8 activation rows share every W word loaded (rows
+//    beyond 8 re-stream W).
+//  * XT = 0 reads packed activation words from global memory.  XT = 1 / 2
+//    take real-valued fp32 / bf16 activation rows and pack them inside the
+//    kernel: each block sign-packs its K-chunk of the (at most 8) rows into
+//    LDS, eight lanes per word as the stand-alone packer does, after the
+//    first W loads and the alpha loads are already in flight.  A batch-1
+//    step is then one launch.
 //  * partial counts are summed across the L lanes with xor-shuffles, the
 //    column totals are gathered in LDS, and the epilogue stores them
 //    coalesced (int32 / alpha-scaled fp32) or ballots 64 of them into one
-//    repacked word (P is chosen so that a step covers 64 columns).
+//    repacked word (P is chosen so that a block step covers 64 columns).
 //  * the last word of K is masked (pad bits never count).
 #include "../../include/bnn.h"
 #include "bnn_internal.h"
+#include "sign_bits.h"
 
 namespace bnn {
 namespace {
 
-constexpr int kMR = 8;  // activation rows sharing one pass over W
+constexpr int kMR = 8;            // activation rows sharing one pass over W
+constexpr int kChunkWords = 512;  // fused packer: K-chunk held in LDS per row
+#ifndef BNN_GEMV_BLOCKS_PER_CU
+#define BNN_GEMV_BLOCKS_PER_CU 8
+#endif
+constexpr int kBlocksPerCU = BNN_GEMV_BLOCKS_PER_CU;  // persistent grid size (x 256 CUs)
 
-template <int EPI, int L, int VEC, int P>
+template <int EPI, int L, int VEC, int P, int XT>
 __global__ void __launch_bounds__(256)
-    gemv_kernel(const uint64_t *__restrict__ xp, const uint64_t *__restrict__ wp,
+    gemv_kernel(const void *__restrict__ xv, int64_t ldx, const uint64_t *__restrict__ wp,
                 const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
-                int kw) {
-  constexpr int G = 64 / L;          // columns per wave per pass
-  constexpr int CB = 4 * G * P;      // columns per block step
+                int kw, int kcw, int xvec) {
+  constexpr int G = 64 / L;      // columns per wave per pass
+  constexpr int CB = 4 * G * P;  // columns per block step
   static_assert(EPI != BNN_EPI_REPACK || CB == 64, "a repack step covers 64 columns");
+  static_assert(256 % CB == 0, "a thread's epilogue column is fixed");
   __shared__ uint32_t res[kMR][CB];
-
+  extern __shared__ __attribute__((aligned(16))) uint64_t xs[];  // XT != 0: [rows][kcw]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int sub = lane / L;
   const int part = lane % L;
-  const int units = kw / VEC;  // VEC == 2 only when kw is even
   const uint64_t tmask = tail_mask(K);
-  const int64_t nb = (int64_t)blockIdx.x * CB;
   const int nw = (N + 63) >> 6;
+  const int nsteps = (N + CB - 1) / CB;
+  const uint64_t *xp = static_cast<const uint64_t *>(xv);
 
-  for (int mb = 0; mb < M; mb += kMR) {
-    const int mrows = (M - mb) < kMR ? (M - mb) : kMR;
-    uint32_t acc[P][kMR];
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int r = 0; r < kMR; ++r) acc[p][r] = 0;
-
-    for (int ub = 0; ub < units; ub += L) {
-      const int u = ub + part;
-      uint64_t w[P][VEC];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
-        const bool ok = (u < units) && (n < N);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) w[p][v] = 0;
-        if (ok) {
-          const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
-          if (VEC == 2) {
-            const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
-            w[p][0] = t.x;
-            w[p][VEC - 1] = t.y;
-          } else {
-            w[p][0] = src[0];
-          }
-        }
+  // Sign-pack activation rows mb .. mb+mrows-1, words c0 .. c0+cw-1 into LDS
+  // (eight lanes per word, as the stand-alone packer does).
+  auto pack_x = [&](int mb, int mrows, int c0, int cw) {
+    const int grp = tid >> 3, t = tid & 7;
+    const int total = mrows * cw;
+    for (int q0 = 0; q0 < total; q0 += 32) {  // uniform trip count
+      const int q = q0 + grp;
+      int n_ok = 0;
+      int64_t e0 = 0;
+      if (q < total) {
+        const int r = q / cw, w = q - r * cw;
+        const int64_t e = (int64_t)(c0 + w) * 64 + 8 * t;
+        const int64_t left = (int64_t)K - e;
+        n_ok = left >= 8 ? 8 : (left > 0 ? (int)left : 0);
+        e0 = (int64_t)(mb + r) * ldx + e;
       }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const int word = u * VEC + v;
-        const uint64_t wm = (word == kw - 1) ? tmask : ~uint64_t(0);
-#pragma unroll
-        for (int r = 0; r < kMR; ++r) {
-          if (r >= mrows) break;
-          const uint64_t x = (u < units) ? (xp[(int64_t)(mb + r) * kw + word] & wm) : 0;
-#pragma unroll
-          for (int p = 0; p < P; ++p) acc[p][r] += (uint32_t)__popcll(x ^ (w[p][v] & wm));
-        }
+      uint32_t byte;
+      if (xvec)
+        byte = sign_byte<(XT == 2 ? 1 : 0), true>(xv, e0, n_ok);
+      else
+        byte = sign_byte<(XT == 2 ? 1 : 0), false>(xv, e0, n_ok);
+      const uint64_t word = word_from_bytes(byte, t);
+      if (t == 0 && q < total) {
+        const int r = q / cw, w = q - r * cw;
+        xs[r * kcw + w] = word;
       }
     }
+  };
 
-    // Sum the L partial counts of each column (all lanes of a group end with the total).
+  // With at most 8 rows and one K-chunk, the packed activations stay in LDS
+  // for every column step of this block: pack them once.
+  const bool x_once = XT != 0 && M <= kMR && kw <= kcw;
+  if constexpr (XT != 0) {
+    if (x_once) {
+      pack_x(0, M, 0, kw);
+      __syncthreads();
+    }
+  }
+
+  for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
+    const int64_t nb = (int64_t)step * CB;
+    // The epilogue column of this thread is fixed (CB divides 256): fetch its
+    // scale now so the load overlaps the W stream.
+    float a_pre = 0.0f;
+    if (EPI == BNN_EPI_SCALED && nb + (tid % CB) < N) a_pre = alpha[nb + (tid % CB)];
+
+    for (int mb = 0; mb < M; mb += kMR) {
+      const int mrows = (M - mb) < kMR ? (M - mb) : kMR;
+      uint32_t acc[P][kMR];
 #pragma unroll
-    for (int p = 0; p < P; ++p)
+      for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int r = 0; r < kMR; ++r) {
-        if (r >= mrows) break;
-        uint32_t a = acc[p][r];
+        for (int r = 0; r < kMR; ++r) acc[p][r] = 0;
+
+      for (int c0 = 0; c0 < kw; c0 += kcw) {
+        const int cw = (kw - c0) < kcw ? (kw - c0) : kcw;
+        const int ubeg = c0 / VEC, uend = (c0 + cw) / VEC;
+
+        uint64_t wa[P][VEC], wb[P][VEC];
+        auto load_w = [&](int ub, uint64_t(&w)[P][VEC]) {
+          const int u = ub + part;
 #pragma unroll
-        for (int off = L / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
-        acc[p][r] = a;
+          for (int p = 0; p < P; ++p) {
+            const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) w[p][v] = 0;
+            if (u < uend && n < N) {
+              const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
+              if (VEC == 2) {
+                const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+                w[p][0] = t.x;
+                w[p][VEC - 1] = t.y;
+              } else {
+                w[p][0] = src[0];
+              }
+            }
+          }
+        };
+        load_w(ubeg, wa);
+
+        if constexpr (XT != 0) {
+          if (!x_once) {
+            __syncthreads();  // the previous chunk's words are consumed
+            pack_x(mb, mrows, c0, cw);
+            __syncthreads();
+          }
+        }
+
+        for (int ub = ubeg; ub < uend; ub += L) {
+          if (ub + L < uend) load_w(ub + L, wb);
+          const int u = ub + part;
+          if (u < uend) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+              const int word = u * VEC + v;
+              const uint64_t wm = (word == kw - 1) ? tmask : ~uint64_t(0);
+#pragma unroll
+              for (int r = 0; r < kMR; ++r) {
+                if (r >= mrows) break;
+                uint64_t x;
+                if constexpr (XT == 0)
+                  x = xp[(int64_t)(mb + r) * kw + word] & wm;
+                else
+                  x = xs[r * kcw + (word - c0)] & wm;
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                  const uint64_t d = x ^ (wa[p][v] & wm);
+                  acc[p][r] = popc_acc((uint32_t)(d >> 32), popc_acc((uint32_t)d, acc[p][r]));
+                }
+              }
+            }
+          }
+#pragma unroll
+          for (int p = 0; p < P; ++p)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) wa[p][v] = wb[p][v];
+        }
       }
-    __syncthreads();  // res is free (previous row block finished its epilogue)
-    if (part == 0) {
+
+      // Sum the L partial counts of each column (all lanes of a group end with the total).
 #pragma unroll
       for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int r = 0; r < kMR; ++r) {
           if (r >= mrows) break;
-          res[r][(p * 4 + wave) * G + sub] = acc[p][r];
+          uint32_t a = acc[p][r];
+#pragma unroll
+          for (int off = L / 2; off >= 1; off >>= 1) a += __shfl_xor(a, off, 64);
+          acc[p][r] = a;
         }
-    }
-    __syncthreads();
-
-    if (EPI == BNN_EPI_REPACK) {
-      if (wave == 0) {
-        const int64_t n = nb + lane;
-        for (int r = 0; r < mrows; ++r) {
-          const int dot = (int)((uint32_t)K - 2u * res[r][lane]);
-          const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= 0);
-          if (lane == 0 && (nb >> 6) < nw)
-            static_cast<uint64_t *>(yv)[(int64_t)(mb + r) * nw + (nb >> 6)] = word;
-        }
+      __syncthreads();  // res is free (the previous epilogue has read it)
+      if (part == 0) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int r = 0; r < kMR; ++r) {
+            if (r >= mrows) break;
+            res[r][(p * 4 + wave) * G + sub] = acc[p][r];
+          }
       }
-    } else {
-      for (int i = tid; i < mrows * CB; i += 256) {
-        const int r = i / CB, c = i - r * CB;
+      __syncthreads();
+
+      if (EPI == BNN_EPI_REPACK) {
+        if (wave == 0) {
+          const int64_t n = nb + lane;
+          for (int r = 0; r < mrows; ++r) {
+            const int dot = (int)((uint32_t)K - 2u * res[r][lane]);
+            const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= 0);
+            if (lane == 0) static_cast<uint64_t *>(yv)[(int64_t)(mb + r) * nw + (nb >> 6)] = word;
+          }
+        }
+      } else {
+        const int c = tid % CB;
         const int64_t n = nb + c;
-        if (n >= N) continue;
-        const int dot = (int)((uint32_t)K - 2u * res[r][c]);
-        const int64_t o = (int64_t)(mb + r) * N + n;
-        if (EPI == BNN_EPI_I32)
-          static_cast<int32_t *>(yv)[o] = dot;
-        else
-          static_cast<float *>(yv)[o] = __fmul_rn((float)dot, alpha[n]);
+        if (n < N) {
+          for (int r = tid / CB; r < mrows; r += 256 / CB) {
+            const int dot = (int)((uint32_t)K - 2u * res[r][c]);
+            const int64_t o = (int64_t)(mb + r) * N + n;
+            if (EPI == BNN_EPI_I32)
+              static_cast<int32_t *>(yv)[o] = dot;
+            else
+              static_cast<float *>(yv)[o] = __fmul_rn((float)dot, a_pre);
+          }
+        }
       }
     }
   }
 }
 
-template <int EPI, int L, int VEC>
-hipError_t launch_l(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
-                    int N, int K, int kw, hipStream_t s) {
-  constexpr int P = (EPI == BNN_EPI_REPACK) ? L / 4 : 1;
+struct Args {
+  const void *x;
+  int64_t ldx;
+  const uint64_t *wp;
+  const float *alpha;
+  void *y;
+  int M, N, K, kw, kcw, xvec;
+};
+
+template <int EPI, int L, int VEC, int XT, int P>
+hipError_t launch_lp(const Args &a, hipStream_t s) {
   constexpr int CB = 4 * (64 / L) * P;
-  const int64_t blocks = ((int64_t)N + CB - 1) / CB;
-  hipLaunchKernelGGL((gemv_kernel<EPI, L, VEC, P>), dim3((unsigned)blocks), dim3(256), 0, s, xp,
-                     wp, alpha, y, M, N, K, kw);
+  const int64_t steps = ((int64_t)a.N + CB - 1) / CB;
+  // Persistent grid: at most kBlocksPerCU blocks per CU, striding over
+  // column steps (so the fused packer runs once per block).
+  const int64_t cap = 256 * kBlocksPerCU;
+  const int64_t blocks = steps < cap ? steps : cap;
+  const int rows = a.M < kMR ? a.M : kMR;
+  const size_t shmem = XT == 0 ? 0 : (size_t)rows * a.kcw * sizeof(uint64_t);
+  hipLaunchKernelGGL((gemv_kernel<EPI, L, VEC, P, XT>), dim3((unsigned)blocks), dim3(256), shmem,
+                     s, a.x, a.ldx, a.wp, a.alpha, a.y, a.M, a.N, a.K, a.kw, a.kcw, a.xvec);
   return hipGetLastError();
 }
 
-template <int EPI, int VEC>
-hipError_t launch_vec(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
-                      int N, int K, int kw, hipStream_t s) {
-  const int units = kw / VEC;
-  if (units <= 4) return launch_l<EPI, 4, VEC>(xp, wp, alpha, y, M, N, K, kw, s);
-  if (units <= 8) return launch_l<EPI, 8, VEC>(xp, wp, alpha, y, M, N, K, kw, s);
-  if (units <= 16) return launch_l<EPI, 16, VEC>(xp, wp, alpha, y, M, N, K, kw, s);
-  if (units <= 32) return launch_l<EPI, 32, VEC>(xp, wp, alpha, y, M, N, K, kw, s);
-  return launch_l<EPI, 64, VEC>(xp, wp, alpha, y, M, N, K, kw, s);
+template <int EPI, int L, int VEC, int XT>
+hipError_t launch_l(const Args &a, hipStream_t s) {
+  if constexpr (EPI == BNN_EPI_REPACK) {
+    return launch_lp<EPI, L, VEC, XT, L / 4>(a, s);  // a step covers 64 columns
+  } else {
+    // One pass per step while one wave of blocks covers N (latency-bound
+    // sizes: more, smaller blocks); four passes beyond that, so each lane
+    // keeps four W loads in flight per step when streaming large W.
+    constexpr int CB1 = 4 * (64 / L);
+    if ((int64_t)a.N <= (int64_t)CB1 * 256 * kBlocksPerCU)
+      return launch_lp<EPI, L, VEC, XT, 1>(a, s);
+    return launch_lp<EPI, L, VEC, XT, 4>(a, s);
+  }
 }
 
-template <int EPI>
-hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
-                      int N, int K, int kw, hipStream_t s) {
-  const bool vec2 = (kw % 2 == 0) && ((uintptr_t)xp % 16 == 0) && ((uintptr_t)wp % 16 == 0);
-  if (vec2) return launch_vec<EPI, 2>(xp, wp, alpha, y, M, N, K, kw, s);
-  return launch_vec<EPI, 1>(xp, wp, alpha, y, M, N, K, kw, s);
+template <int EPI, int VEC, int XT>
+hipError_t launch_vec(const Args &a, hipStream_t s) {
+  const int units = a.kw / VEC;
+  if (units <= 4) return launch_l<EPI, 4, VEC, XT>(a, s);
+  if (units <= 8) return launch_l<EPI, 8, VEC, XT>(a, s);
+  if (units <= 16) return launch_l<EPI, 16, VEC, XT>(a, s);
+  if (units <= 32) return launch_l<EPI, 32, VEC, XT>(a, s);
+  return launch_l<EPI, 64, VEC, XT>(a, s);
+}
+
+template <int EPI, int XT>
+hipError_t launch_epi(const Args &a, hipStream_t s) {
+  const bool x16 = XT != 0 || ((uintptr_t)a.x % 16 == 0);
+  const bool vec2 = (a.kw % 2 == 0) && x16 && ((uintptr_t)a.wp % 16 == 0);
+  if (vec2) return launch_vec<EPI, 2, XT>(a, s);
+  return launch_vec<EPI, 1, XT>(a, s);
+}
+
+template <int XT>
+hipError_t launch_xt(const Args &a, int epilogue, hipStream_t s) {
+  switch (epilogue) {
+    case BNN_EPI_I32: return launch_epi<BNN_EPI_I32, XT>(a, s);
+    case BNN_EPI_SCALED: return launch_epi<BNN_EPI_SCALED, XT>(a, s);
+    default: return launch_epi<BNN_EPI_REPACK, XT>(a, s);
+  }
 }
 
 }  // namespace
@@ -173,14 +303,22 @@ hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const float *alpha
 hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
                        int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s) {
   const int kw = (int)((K + 63) / 64);
-  switch (epilogue) {
-    case BNN_EPI_I32:
-      return launch_epi<BNN_EPI_I32>(xp, wp, alpha, y, (int)M, (int)N, (int)K, kw, s);
-    case BNN_EPI_SCALED:
-      return launch_epi<BNN_EPI_SCALED>(xp, wp, alpha, y, (int)M, (int)N, (int)K, kw, s);
-    default:
-      return launch_epi<BNN_EPI_REPACK>(xp, wp, alpha, y, (int)M, (int)N, (int)K, kw, s);
-  }
+  const Args a{xp, kw, wp, alpha, y, (int)M, (int)N, (int)K, kw, kw > 0 ? kw : 1, 0};
+  return launch_xt<0>(a, epilogue, s);
+}
+
+hipError_t launch_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
+                           const float *alpha, void *y, int64_t M, int64_t N, int64_t K,
+                           int epilogue, hipStream_t s) {
+  const int kw = (int)((K + 63) / 64);
+  const int64_t esize = dtype == 0 ? 4 : 2;
+  // 16-byte activation loads need every row start 16-byte aligned.
+  const int xvec = ((uintptr_t)x % 16 == 0) && ((ldx * esize) % 16 == 0 || M == 1);
+  // K-chunk per row in LDS: even (for 16-byte W loads), at most kChunkWords.
+  int kcw = kw < kChunkWords ? kw : kChunkWords;
+  if (kcw < 1) kcw = 1;
+  const Args a{x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, kw, kcw, xvec};
+  return dtype == 0 ? launch_xt<1>(a, epilogue, s) : launch_xt<2>(a, epilogue, s);
 }
 
 }  // namespace bnn

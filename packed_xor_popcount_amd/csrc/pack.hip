@@ -16,53 +16,12 @@
 // long ones.  The element of a word past K (the tail) and rows whose start is
 // not 16-byte aligned fall back to guarded element loads.
 #include "bnn_internal.h"
+#include "sign_bits.h"
 
 namespace bnn {
 namespace {
 
-// Projection on the bit pattern, so flush-to-zero can never flip a sign.
-// fp32: the value is > 0 exactly when 0 < (int32)b <= 0x7F800000 (positive
-// subnormal, normal or +inf); -0, +0, NaN and negatives are not.
-__device__ __forceinline__ uint32_t minus_f32(uint32_t b) { return (b - 1u) >= 0x7F800000u; }
-// bf16 is the upper half of an fp32 pattern: the same test on 16 bits.
-__device__ __forceinline__ uint32_t minus_bf16(uint32_t h) { return ((h - 1u) & 0xFFFFu) >= 0x7F80u; }
-
 constexpr int kSub = 4;  // words per lane group in flight
-
-template <int DT>
-__device__ __forceinline__ uint32_t load_elem(const void *src, int64_t i) {
-  if (DT == 0) return static_cast<const uint32_t *>(src)[i];
-  return static_cast<const uint16_t *>(src)[i];
-}
-
-// Sign byte of the 8 elements starting at element index `e0` of the flat
-// source; `n_ok` of them (0..8) exist, the rest contribute 0 (pad) bits.
-template <int DT, bool VEC>
-__device__ __forceinline__ uint32_t sign_byte(const void *src, int64_t e0, int n_ok) {
-  uint32_t b = 0;
-  if (VEC && n_ok == 8) {
-    if (DT == 0) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint32_t *>(src) + e0);
-      const uint4 a = p[0], c = p[1];
-      b = minus_f32(a.x) | minus_f32(a.y) << 1 | minus_f32(a.z) << 2 | minus_f32(a.w) << 3 |
-          minus_f32(c.x) << 4 | minus_f32(c.y) << 5 | minus_f32(c.z) << 6 | minus_f32(c.w) << 7;
-    } else {
-      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + e0);
-      b = minus_bf16(a.x & 0xFFFFu) | minus_bf16(a.x >> 16) << 1 | minus_bf16(a.y & 0xFFFFu) << 2 |
-          minus_bf16(a.y >> 16) << 3 | minus_bf16(a.z & 0xFFFFu) << 4 |
-          minus_bf16(a.z >> 16) << 5 | minus_bf16(a.w & 0xFFFFu) << 6 | minus_bf16(a.w >> 16) << 7;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (e < n_ok) {
-        const uint32_t v = load_elem<DT>(src, e0 + e);
-        b |= (DT == 0 ? minus_f32(v) : minus_bf16(v)) << e;
-      }
-    }
-  }
-  return b;
-}
 
 template <int DT, bool VEC>
 __global__ void __launch_bounds__(256)
@@ -95,12 +54,9 @@ __global__ void __launch_bounds__(256)
     }
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
-      uint32_t v = byte[s] << (8 * (t & 3));
-      v |= __shfl_xor(v, 1, 64);
-      v |= __shfl_xor(v, 2, 64);
-      const uint32_t hi = __shfl_xor(v, 4, 64);
+      const uint64_t word = word_from_bytes(byte[s], t);
       const int64_t g = g0 + s * 8 + grp;
-      if (t == 0 && g < total) dst[g] = (uint64_t)v | ((uint64_t)hi << 32);
+      if (t == 0 && g < total) dst[g] = word;
     }
   }
 }

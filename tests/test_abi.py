@@ -84,6 +84,7 @@ def test_gemm_validation(lib):
     g = lib.bnn_gemm_ex
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 3, 0, None) == E_ARG
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 0, 9, None) == E_ARG
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, 2 ** 24 + 1, 0, 3, None) == E_SHAPE  # MFMA K limit
     assert g(FAKE, FAKE, FAKE, FAKE, -1, 1, 1, 0, 0, None) == E_SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, 1, -1, 1, 0, 0, None) == E_SHAPE
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 1, -1, 0, 0, None) == E_SHAPE
@@ -116,3 +117,19 @@ def test_binding_rejects_cpu_tensors():
         bnn.pack_signs(torch.zeros(2, 3))
     with pytest.raises(TypeError):
         bnn.gemm_u64(torch.zeros(2, 1, dtype=torch.int64), torch.zeros(2, 1, dtype=torch.int64), 3)
+
+
+def test_gemv_act_validation(lib):
+    f = lib.bnn_gemv_act
+    assert f(FAKE, 5, 4, FAKE, FAKE, FAKE, 1, 1, 4, 0, None) == E_DTYPE
+    assert f(FAKE, 0, 4, FAKE, FAKE, FAKE, 1, 1, 4, 7, None) == E_ARG
+    assert f(FAKE, 0, 3, FAKE, FAKE, FAKE, 1, 1, 4, 0, None) == E_SHAPE    # ldx < K
+    assert f(FAKE, 0, 4, FAKE, FAKE, FAKE, -1, 1, 4, 0, None) == E_SHAPE
+    assert f(None, 0, 4, FAKE, FAKE, FAKE, 1, 1, 4, 0, None) == E_NULL
+    assert f(FAKE, 0, 4, None, FAKE, FAKE, 1, 1, 4, 0, None) == E_NULL
+    assert f(FAKE, 0, 4, FAKE, None, FAKE, 1, 1, 4, 1, None) == E_NULL
+    assert f(P(0x1002), 0, 4, FAKE, FAKE, FAKE, 1, 1, 4, 0, None) == E_ALIGN   # fp32 x
+    assert f(P(0x1001), 1, 4, FAKE, FAKE, FAKE, 1, 1, 4, 0, None) == E_ALIGN   # bf16 x
+    assert f(FAKE, 1, 4, FAKE_ODD, FAKE, FAKE, 1, 1, 4, 0, None) == E_ALIGN
+    assert f(FAKE, 1, 4, FAKE, FAKE, P(0x1004), 1, 1, 4, 2, None) == E_ALIGN
+    assert f(None, 0, 4, FAKE, None, None, 0, 3, 4, 0, None) == OK

@@ -26,7 +26,7 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-ALGOS = [bnn.ALGO_GEMV, bnn.ALGO_TILED, bnn.ALGO_AUTO]
+ALGOS = [bnn.ALGO_GEMV, bnn.ALGO_TILED, bnn.ALGO_MFMA, bnn.ALGO_AUTO]
 
 
 def say(*a):
@@ -307,3 +307,78 @@ def test_workload_chain_65536():
     assert_scaled_equal(y.cpu().numpy()[rows], final)
     # property at every row: hidden words have zero pad bits and the right shape
     assert h1.shape == (x.shape[0], 4) and h2.shape == (x.shape[0], 2)
+
+
+# ---------------------------------------------------------------------------
+# bnn_gemv_act: activation packing fused into the weight-streaming product
+
+ACT_SHAPES = [(1, 1, 1), (1, 256, 512), (1, 4096, 4096), (3, 100, 65), (8, 300, 1000),
+              (9, 77, 129), (20, 64, 4095), (2, 130, 40000), (1, 50, 70001), (5, 1000, 0)]
+
+
+@pytest.mark.parametrize("M,N,K", ACT_SHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gemv_act_parity(M, N, K, dtype):
+    say("gemv_act", M, N, K, dtype)
+    c = workloads.random_case(seed=M * 31 + N * 7 + K, M=M, N=N, K=K, dist="normal",
+                              zero_frac=0.01 if M * K >= 2 else 0.0, dtype=dtype)
+    x, K = c["x"], c["K"]
+    rng = np.random.default_rng(K + 1)
+    wg, wc = rand_packed(rng, N, K)
+    alpha = c["alpha"]
+    xd, wd, ad = x.to(DEV), to_dev_words(wg), alpha.to(DEV)
+    rx = oracle.pack(host_input(x), k=K) if M else np.zeros((0, oracle.words(K)), np.uint64)
+    assert np.array_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_I32).cpu().numpy(),
+                          oracle.gemm_i32(rx, wc, K))
+    assert_scaled_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_SCALED, alpha=ad).cpu().numpy(),
+                        oracle.gemm_scaled(rx, wc, alpha.numpy(), K))
+    assert np.array_equal(words_np(bnn.gemv_act(xd, wd, K, bnn.EPI_REPACK)),
+                          oracle.sign_repack(rx, wc, K))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gemv_act_strided_rows(dtype):
+    # row stride 1003 elements (not a multiple of 16 bytes): guarded loads
+    g = workloads.generator(31)
+    big = workloads.normal(g, 4, 1003).to(dtype)
+    x = big[:, :900]
+    rng = np.random.default_rng(31)
+    wg, wc = rand_packed(rng, 70, 900)
+    rx = oracle.pack(np.ascontiguousarray(host_input(big)[:, :900]))
+    got = bnn.gemv_act(big.to(DEV)[:, :900], to_dev_words(wg), 900, bnn.EPI_I32).cpu().numpy()
+    assert np.array_equal(got, oracle.gemm_i32(rx, wc, 900))
+    assert x.shape == (4, 900)
+
+
+def test_gemv_act_workload_gemv_4096():
+    # the benchmark's one-launch step: bf16 x packed in-kernel, alpha-scaled output
+    d = workloads.make("gemv_4096")
+    wp = bnn.pack_signs(d["w"].to(DEV))
+    y = bnn.gemv_act(d["x"].to(DEV), wp, d["K"], bnn.EPI_SCALED, alpha=d["alpha"].to(DEV))
+    rx, rw = oracle.pack(workloads.bf16_bits(d["x"])), oracle.pack(d["w"].numpy())
+    assert_scaled_equal(y.cpu().numpy(), oracle.gemm_scaled(rx, rw, d["alpha"].numpy(), d["K"]))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 20000, 4096), (3, 140000, 200), (2, 40000, 1000),
+                                   (1, 70000, 130)])
+def test_gemv_many_columns(M, N, K):
+    # N beyond one wave of persistent blocks: the four-pass step and the
+    # grid-stride loop of the GEMV kernel, packed and fused activations
+    say("gemv many columns", M, N, K)
+    c = workloads.random_case(seed=N + K, M=M, N=N, K=K, dist="normal", dtype=torch.bfloat16)
+    rng = np.random.default_rng(N)
+    wg, wc = rand_packed(rng, N, K)
+    rx = oracle.pack(host_input(c["x"]))
+    alpha = c["alpha"]
+    xd, wd, ad = c["x"].to(DEV), to_dev_words(wg), alpha.to(DEV)
+    xpd = to_dev_words(rx)
+    ref = oracle.gemm_i32(rx, wc, K)
+    refs = oracle.gemm_scaled(rx, wc, alpha.numpy(), K)
+    refp = oracle.sign_repack(rx, wc, K)
+    assert np.array_equal(bnn.gemm_ex(xpd, wd, K, bnn.EPI_I32, bnn.ALGO_GEMV).cpu().numpy(), ref)
+    assert_scaled_equal(bnn.gemm_ex(xpd, wd, K, bnn.EPI_SCALED, bnn.ALGO_GEMV, alpha=ad)
+                        .cpu().numpy(), refs)
+    assert np.array_equal(words_np(bnn.gemm_ex(xpd, wd, K, bnn.EPI_REPACK, bnn.ALGO_GEMV)), refp)
+    assert np.array_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_I32).cpu().numpy(), ref)
+    assert_scaled_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_SCALED, alpha=ad).cpu().numpy(), refs)
+    assert np.array_equal(words_np(bnn.gemv_act(xd, wd, K, bnn.EPI_REPACK)), refp)
