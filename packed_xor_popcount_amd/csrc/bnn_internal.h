@@ -47,4 +47,19 @@ __device__ __forceinline__ uint32_t popc_acc(uint32_t v, uint32_t acc) {
   return r;
 }
 
+// Sum of v over aligned groups of L lanes (L a power of two, 1..64); every
+// lane of a group receives the group total.  Within a row of 16 lanes the
+// exchanges are DPP moves (quad permutes, half-row and row mirrors: VALU
+// latency); only the steps across rows use ds_swizzle / a lane permute.
+template <int L>
+__device__ __forceinline__ uint32_t group_sum(uint32_t v) {
+  if (L >= 2) v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  if (L >= 4) v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  if (L >= 8) v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  if (L >= 16) v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false); // row_mirror
+  if (L >= 32) v += (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);              // lane ^ 16
+  if (L >= 64) v += (uint32_t)__shfl_xor((int)v, 32, 64);
+  return v;
+}
+
 }  // namespace bnn

@@ -64,12 +64,18 @@ __global__ void __launch_bounds__(256)
   const uint64_t *xp = static_cast<const uint64_t *>(xv);
 
   // Sign-pack activation rows mb .. mb+mrows-1, words c0 .. c0+cw-1 into LDS
-  // (eight lanes per word, as the stand-alone packer does).
-  auto pack_x = [&](int mb, int mrows, int c0, int cw) {
+  // (eight lanes per word, as the stand-alone packer does; each lane group
+  // builds up to kS words per round with all their loads in flight).  The
+  // load and finish halves of a round are separate so that the first round
+  // can be loaded before the W stream starts and finished after it.
+  constexpr int kS = 4;
+  constexpr int DTX = XT == 2 ? 1 : 0;
+  auto pack_load = [&](int mb, int mrows, int c0, int cw, int q0, Raw8(&raw)[kS]) {
     const int grp = tid >> 3, t = tid & 7;
     const int total = mrows * cw;
-    for (int q0 = 0; q0 < total; q0 += 32) {  // uniform trip count
-      const int q = q0 + grp;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const int q = q0 + s * 32 + grp;
       int n_ok = 0;
       int64_t e0 = 0;
       if (q < total) {
@@ -79,35 +85,46 @@ __global__ void __launch_bounds__(256)
         n_ok = left >= 8 ? 8 : (left > 0 ? (int)left : 0);
         e0 = (int64_t)(mb + r) * ldx + e;
       }
-      uint32_t byte;
       if (xvec)
-        byte = sign_byte<(XT == 2 ? 1 : 0), true>(xv, e0, n_ok);
+        raw[s] = load_raw8<DTX, true>(xv, e0, n_ok);
       else
-        byte = sign_byte<(XT == 2 ? 1 : 0), false>(xv, e0, n_ok);
-      const uint64_t word = word_from_bytes(byte, t);
+        raw[s] = load_raw8<DTX, false>(xv, e0, n_ok);
+    }
+  };
+  auto pack_finish = [&](int mrows, int cw, int q0, const Raw8(&raw)[kS]) {
+    const int grp = tid >> 3, t = tid & 7;
+    const int total = mrows * cw;
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const int q = q0 + s * 32 + grp;
+      const uint64_t word = word_from_bytes(byte_of<DTX>(raw[s]), t);
       if (t == 0 && q < total) {
         const int r = q / cw, w = q - r * cw;
         xs[r * kcw + w] = word;
       }
     }
   };
-
-  // With at most 8 rows and one K-chunk, the packed activations stay in LDS
-  // for every column step of this block: pack them once.
-  const bool x_once = XT != 0 && M <= kMR && kw <= kcw;
-  if constexpr (XT != 0) {
-    if (x_once) {
-      pack_x(0, M, 0, kw);
-      __syncthreads();
+  auto pack_x = [&](int mb, int mrows, int c0, int cw) {
+    for (int q0 = 0; q0 < mrows * cw; q0 += 32 * kS) {  // uniform trip count
+      Raw8 raw[kS];
+      pack_load(mb, mrows, c0, cw, q0, raw);
+      pack_finish(mrows, cw, q0, raw);
     }
-  }
+  };
+  // With at most 8 rows and one K-chunk, the packed activations stay in LDS
+  // for every column step of this block: they are packed once, right after
+  // the first step's W loads are issued (so the two latencies overlap).
+  const bool x_once = XT != 0 && M <= kMR && kw <= kcw;
+  bool x_ready = false;
 
   for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
     const int64_t nb = (int64_t)step * CB;
-    // The epilogue column of this thread is fixed (CB divides 256): fetch its
-    // scale now so the load overlaps the W stream.
+    // W and alpha are read from clamped, always in-bounds addresses: the loads
+    // are unconditional (no zero-initialised destination registers for the
+    // compiler to guard with waits), W first; lanes whose unit is past the
+    // chunk skip the popcounts and columns past N are never stored.
+    uint64_t wa[P][VEC], wb[P][VEC];
     float a_pre = 0.0f;
-    if (EPI == BNN_EPI_SCALED && nb + (tid % CB) < N) a_pre = alpha[nb + (tid % CB)];
 
     for (int mb = 0; mb < M; mb += kMR) {
       const int mrows = (M - mb) < kMR ? (M - mb) : kMR;
@@ -119,32 +136,41 @@ __global__ void __launch_bounds__(256)
 
       for (int c0 = 0; c0 < kw; c0 += kcw) {
         const int cw = (kw - c0) < kcw ? (kw - c0) : kcw;
-        const int ubeg = c0 / VEC, uend = (c0 + cw) / VEC;
+        const int ubeg = c0 / VEC, uend = (c0 + cw) / VEC;  // uend > ubeg
 
-        uint64_t wa[P][VEC], wb[P][VEC];
         auto load_w = [&](int ub, uint64_t(&w)[P][VEC]) {
-          const int u = ub + part;
+          int u = ub + part;
+          u = u < uend ? u : uend - 1;
 #pragma unroll
           for (int p = 0; p < P; ++p) {
-            const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) w[p][v] = 0;
-            if (u < uend && n < N) {
-              const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
-              if (VEC == 2) {
-                const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
-                w[p][0] = t.x;
-                w[p][VEC - 1] = t.y;
-              } else {
-                w[p][0] = src[0];
-              }
+            int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+            n = n < N ? n : N - 1;
+            const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
+            if (VEC == 2) {
+              const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+              w[p][0] = t.x;
+              w[p][VEC - 1] = t.y;
+            } else {
+              w[p][0] = src[0];
             }
           }
         };
         load_w(ubeg, wa);
+        if (EPI == BNN_EPI_SCALED) {
+          // The epilogue column of this thread is fixed (CB divides 256).
+          int64_t n = nb + (tid % CB);
+          n = n < N ? n : N - 1;
+          a_pre = alpha[n];
+        }
 
         if constexpr (XT != 0) {
-          if (!x_once) {
+          if (x_once) {
+            if (!x_ready) {  // uniform
+              pack_x(0, M, 0, kw);
+              __syncthreads();
+              x_ready = true;
+            }
+          } else {
             __syncthreads();  // the previous chunk's words are consumed
             pack_x(mb, mrows, c0, cw);
             __syncthreads();
@@ -232,6 +258,172 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Batch-1 decode form of the fused kernel: activation rows given as real
+// values (M <= 8, DT 0 = fp32, 1 = bf16, K a multiple of 64, rows 16-byte
+// aligned), and every lane holds at most one unit (VEC words) of each W row
+// it serves (units <= L), so a block step is
+// one straight-line round: issue the W loads, then the activation loads
+// (first step of the block only), then the scale; pack the activations into
+// LDS while the W words are in flight; popcounts; reduction; epilogue.  The
+// same arithmetic and epilogues as gemv_kernel.
+template <int EPI, int L, int VEC, int P, int DT>
+__global__ void __launch_bounds__(256)
+    gemv_act_kernel(const void *__restrict__ xv, int64_t ldx, const uint64_t *__restrict__ wp,
+                    const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
+                    int kw) {
+  constexpr int G = 64 / L;
+  constexpr int CB = 4 * G * P;
+  constexpr int kS = 4;  // activation words per lane group per round
+  static_assert(EPI != BNN_EPI_REPACK || CB == 64, "a repack step covers 64 columns");
+  __shared__ uint32_t res[kMR][CB];
+  extern __shared__ __attribute__((aligned(16))) uint64_t xs[];  // [M][kw]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane / L;
+  const int part = lane % L;
+  const int grp = tid >> 3, t8 = tid & 7;
+  const int nw = (N + 63) >> 6;
+  const int nsteps = (N + CB - 1) / CB;
+  const int units = kw / VEC;   // >= 1 (K > 0 here)
+  const bool u_ok = part < units;
+  const int u = u_ok ? part : units - 1;
+  const int total = M * kw;     // activation words to pack
+
+  // Every activation row holds whole 16-byte-aligned groups of 8 elements
+  // (the launcher checks this), so the loads are unconditional vector loads;
+  // slots past the last word re-read the last one and are not stored.
+  auto x_round = [&](int q0, Raw8(&raw)[kS]) {
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      int q = q0 + s * 32 + grp;
+      q = q < total ? q : total - 1;
+      const int r = q / kw, wd = q - r * kw;
+      const int64_t e0 = (int64_t)r * ldx + (int64_t)wd * 64 + 8 * t8;
+      raw[s] = load_raw8<DT, true>(xv, e0, 8);
+    }
+  };
+  auto x_store = [&](int q0, const Raw8(&raw)[kS]) {
+#pragma unroll
+    for (int s = 0; s < kS; ++s) {
+      const int q = q0 + s * 32 + grp;
+      const uint64_t word = word_from_bytes(byte_of<DT>(raw[s]), t8);
+      if (t8 == 0 && q < total) xs[q] = word;  // row r, word w at r * kw + w == q
+    }
+  };
+
+  bool first = true;
+  for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
+    const int64_t nb = (int64_t)step * CB;
+    uint64_t w[P][VEC];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+      n = n < N ? n : N - 1;
+      const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
+      if (VEC == 2) {
+        const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(src);
+        w[p][0] = v.x;
+        w[p][VEC - 1] = v.y;
+      } else {
+        w[p][0] = src[0];
+      }
+    }
+    if (first) {  // uniform: pack the activations once per block
+      Raw8 raw[kS];
+      x_round(0, raw);
+      x_store(0, raw);
+      for (int q0 = 32 * kS; q0 < total; q0 += 32 * kS) {
+        x_round(q0, raw);
+        x_store(q0, raw);
+      }
+      __syncthreads();
+      first = false;
+    }
+    // Scales of the columns this lane will store (int32 / scaled epilogues
+    // store from the reducing lanes directly).
+    float a_pre[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      a_pre[p] = 0.0f;
+      if (EPI == BNN_EPI_SCALED) {
+        int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+        n = n < N ? n : N - 1;
+        a_pre[p] = alpha[n];
+      }
+    }
+
+    uint32_t acc[P][kMR];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int r = 0; r < kMR; ++r) acc[p][r] = 0;
+    if (u_ok) {  // K is a multiple of 64: no tail word to mask
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const int word = u * VEC + v;
+#pragma unroll
+        for (int r = 0; r < kMR; ++r) {
+          if (r >= M) break;
+          const uint64_t x = xs[r * kw + word];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const uint64_t d = x ^ w[p][v];
+            acc[p][r] = popc_acc((uint32_t)(d >> 32), popc_acc((uint32_t)d, acc[p][r]));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int r = 0; r < kMR; ++r) {
+        if (r >= M) break;
+        acc[p][r] = group_sum<L>(acc[p][r]);
+      }
+
+    if (EPI == BNN_EPI_REPACK) {
+      __syncthreads();  // res is free (the previous step's epilogue has read it)
+      if (part == 0) {
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int r = 0; r < kMR; ++r) {
+            if (r >= M) break;
+            res[r][(p * 4 + wave) * G + sub] = acc[p][r];
+          }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int64_t n = nb + lane;
+        for (int r = 0; r < M; ++r) {
+          const int dot = (int)((uint32_t)K - 2u * res[r][lane]);
+          const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= 0);
+          if (lane == 0) static_cast<uint64_t *>(yv)[(int64_t)r * nw + (nb >> 6)] = word;
+        }
+      }
+    } else if (part == 0) {
+      // Every lane of a group holds its column's total: the first one stores.
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < kMR; ++r) {
+          if (r >= M) break;
+          const int dot = (int)((uint32_t)K - 2u * acc[p][r]);
+          const int64_t o = (int64_t)r * N + n;
+          if (EPI == BNN_EPI_I32)
+            static_cast<int32_t *>(yv)[o] = dot;
+          else
+            static_cast<float *>(yv)[o] = __fmul_rn((float)dot, a_pre[p]);
+        }
+      }
+    }
+  }
+}
+
 struct Args {
   const void *x;
   int64_t ldx;
@@ -250,6 +442,16 @@ hipError_t launch_lp(const Args &a, hipStream_t s) {
   const int64_t cap = 256 * kBlocksPerCU;
   const int64_t blocks = steps < cap ? steps : cap;
   const int rows = a.M < kMR ? a.M : kMR;
+  if constexpr (XT != 0) {
+    // Batch-1 decode form: at most 8 rows and at most one unit per lane.
+    if (a.M <= kMR && a.kw > 0 && a.kw / VEC <= L && a.K % 64 == 0 && a.xvec) {
+      const size_t shmem = (size_t)a.M * a.kw * sizeof(uint64_t);
+      hipLaunchKernelGGL((gemv_act_kernel<EPI, L, VEC, P, XT - 1>), dim3((unsigned)blocks),
+                         dim3(256), shmem, s, a.x, a.ldx, a.wp, a.alpha, a.y, a.M, a.N, a.K,
+                         a.kw);
+      return hipGetLastError();
+    }
+  }
   const size_t shmem = XT == 0 ? 0 : (size_t)rows * a.kcw * sizeof(uint64_t);
   hipLaunchKernelGGL((gemv_kernel<EPI, L, VEC, P, XT>), dim3((unsigned)blocks), dim3(256), shmem,
                      s, a.x, a.ldx, a.wp, a.alpha, a.y, a.M, a.N, a.K, a.kw, a.kcw, a.xvec);

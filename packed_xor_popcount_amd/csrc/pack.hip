@@ -37,9 +37,9 @@ __global__ void __launch_bounds__(256)
   for (int64_t g0 = wave * (8 * kSub); g0 < total; g0 += nwaves * (8 * kSub)) {
     const int64_t row0 = g0 / kw;            // wave-uniform
     const uint32_t w0 = (uint32_t)(g0 - row0 * kw);
-    uint32_t byte[kSub];
+    Raw8 raw[kSub];
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) {
+    for (int s = 0; s < kSub; ++s) {  // all loads first
       const uint32_t tw = w0 + (uint32_t)(s * 8 + grp);
       const uint32_t dr = tw / ukw;
       const int64_t row = row0 + dr;
@@ -50,8 +50,11 @@ __global__ void __launch_bounds__(256)
         const int64_t left = k - e;
         n_ok = left >= 8 ? 8 : (left > 0 ? (int)left : 0);
       }
-      byte[s] = sign_byte<DT, VEC>(src, row * ld + e, n_ok);
+      raw[s] = load_raw8<DT, VEC>(src, row * ld + e, n_ok);
     }
+    uint32_t byte[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) byte[s] = byte_of<DT>(raw[s]);
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
       const uint64_t word = word_from_bytes(byte[s], t);

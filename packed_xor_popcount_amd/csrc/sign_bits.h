@@ -20,46 +20,75 @@ __device__ __forceinline__ uint32_t minus_bf16(uint32_t h) {
   return ((h - 1u) & 0xFFFFu) >= 0x7F80u;
 }
 
-// Sign byte of the 8 elements starting at flat element index e0 of `src`
-// (DT 0: fp32, 1: bf16): element e -> bit e.  Only the first n_ok (0..8)
-// elements exist; the others are not read and give 0 (pad) bits.  VEC: the
-// 8 elements are 16-byte aligned, read with 16-byte loads when all exist.
+// Raw bit patterns of 8 consecutive elements (fp32: 8 words; bf16: 8 halves
+// packed two per word in lo..hi order).  Loading is split from the sign test
+// so that a caller can put several of these loads in flight before using
+// any of them.
+struct Raw8 {
+  uint4 a, b;  // fp32: a = elements 0-3, b = 4-7; bf16: a = elements 0-7
+};
+
+// Load the 8 elements starting at flat element index e0 of `src` (DT 0:
+// fp32, 1: bf16).  Only the first n_ok (0..8) exist; the others are not read
+// and are given the pattern of +1.0 (they become 0, i.e. pad, bits).  VEC:
+// the 8 elements are 16-byte aligned and are read with 16-byte loads when all
+// of them exist.
 template <int DT, bool VEC>
-__device__ __forceinline__ uint32_t sign_byte(const void *src, int64_t e0, int n_ok) {
-  uint32_t b = 0;
+__device__ __forceinline__ Raw8 load_raw8(const void *src, int64_t e0, int n_ok) {
+  Raw8 r;
   if (VEC && n_ok == 8) {
     if (DT == 0) {
       const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint32_t *>(src) + e0);
-      const uint4 a = p[0], c = p[1];
-      b = minus_f32(a.x) | minus_f32(a.y) << 1 | minus_f32(a.z) << 2 | minus_f32(a.w) << 3 |
-          minus_f32(c.x) << 4 | minus_f32(c.y) << 5 | minus_f32(c.z) << 6 | minus_f32(c.w) << 7;
+      r.a = p[0];
+      r.b = p[1];
     } else {
-      const uint4 a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + e0);
-      b = minus_bf16(a.x & 0xFFFFu) | minus_bf16(a.x >> 16) << 1 | minus_bf16(a.y & 0xFFFFu) << 2 |
-          minus_bf16(a.y >> 16) << 3 | minus_bf16(a.z & 0xFFFFu) << 4 |
-          minus_bf16(a.z >> 16) << 5 | minus_bf16(a.w & 0xFFFFu) << 6 | minus_bf16(a.w >> 16) << 7;
+      r.a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + e0);
+      r.b = make_uint4(0, 0, 0, 0);
     }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (e < n_ok) {
-        const uint32_t v = DT == 0 ? static_cast<const uint32_t *>(src)[e0 + e]
-                                   : (uint32_t) static_cast<const uint16_t *>(src)[e0 + e];
-        b |= (DT == 0 ? minus_f32(v) : minus_bf16(v)) << e;
-      }
-    }
+    return r;
   }
-  return b;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (DT == 0)
+      v[e] = e < n_ok ? static_cast<const uint32_t *>(src)[e0 + e] : 0x3F800000u;
+    else
+      v[e] = e < n_ok ? (uint32_t) static_cast<const uint16_t *>(src)[e0 + e] : 0x3F80u;
+  }
+  if (DT == 0) {
+    r.a = make_uint4(v[0], v[1], v[2], v[3]);
+    r.b = make_uint4(v[4], v[5], v[6], v[7]);
+  } else {
+    r.a = make_uint4(v[0] | v[1] << 16, v[2] | v[3] << 16, v[4] | v[5] << 16, v[6] | v[7] << 16);
+    r.b = make_uint4(0, 0, 0, 0);
+  }
+  return r;
+}
+
+// Sign byte of 8 loaded elements: element e -> bit e (1 when it projects to -1).
+template <int DT>
+__device__ __forceinline__ uint32_t byte_of(const Raw8 &r) {
+  if (DT == 0)
+    return minus_f32(r.a.x) | minus_f32(r.a.y) << 1 | minus_f32(r.a.z) << 2 |
+           minus_f32(r.a.w) << 3 | minus_f32(r.b.x) << 4 | minus_f32(r.b.y) << 5 |
+           minus_f32(r.b.z) << 6 | minus_f32(r.b.w) << 7;
+  return minus_bf16(r.a.x & 0xFFFFu) | minus_bf16(r.a.x >> 16) << 1 |
+         minus_bf16(r.a.y & 0xFFFFu) << 2 | minus_bf16(r.a.y >> 16) << 3 |
+         minus_bf16(r.a.z & 0xFFFFu) << 4 | minus_bf16(r.a.z >> 16) << 5 |
+         minus_bf16(r.a.w & 0xFFFFu) << 6 | minus_bf16(r.a.w >> 16) << 7;
 }
 
 // Assemble the bytes of 8 consecutive lanes (lane & 7 == t holds the byte for
 // bits 8t .. 8t+7) into one 64-bit word.  Every lane of the wave must call it
-// (it shuffles); the word is valid in the lane with t == 0.
+// (it exchanges registers across lanes); the word is valid in the lane with
+// t == 0.  The exchanges are DPP moves: two quad permutes OR the four bytes
+// of each quad into a dword, and a half-row mirror hands lane 0 of the group
+// the dword of lanes 4-7 (from lane 7).
 __device__ __forceinline__ uint64_t word_from_bytes(uint32_t byte, int t) {
   uint32_t v = byte << (8 * (t & 3));
-  v |= __shfl_xor(v, 1, 64);
-  v |= __shfl_xor(v, 2, 64);
-  const uint32_t hi = __shfl_xor(v, 4, 64);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // half mirror
   return (uint64_t)v | ((uint64_t)hi << 32);
 }
 
