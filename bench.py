@@ -66,6 +66,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="gemv: launch the steps one by one instead of replaying a HIP graph "
+                         "(for counter collection)")
+    ap.add_argument("--calibrate-copy", type=int, default=None, metavar="MIB",
+                    help="run 8 plain device copies of MIB MiB and exit (the reference kernel "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -84,6 +90,40 @@ def timed(fn, n, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n
+
+
+def kernel_sources_digest(names):
+    """sha256 over the library sources a counter record was taken with."""
+    import hashlib
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "packed_xor_popcount_amd",
+                        "csrc")
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(root, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(profile_name, sources):
+    """HBM bytes per launch from a committed counter summary under profiles/
+    (FETCH_SIZE + WRITE_SIZE of the kernel, each scaled by the same counter's
+    reading for a plain copy of known size).  None when the summary is
+    missing or was taken with different kernel sources."""
+    import re
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", profile_name)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_sources_digest(sources):
+        return None
+    return float(t.group(1))
+
+
+GEMV_SOURCES = ["gemv.hip", "sign_bits.h", "bnn_internal.h"]
+MFMA_SOURCES = ["gemm_mfma.hip", "bnn_internal.h"]
 
 
 def gemv_leg(args, steps, warmup):
@@ -131,21 +171,24 @@ def gemv_leg(args, steps, warmup):
         torch.cuda.synchronize()
         return gr
 
-    full, rem = divmod(steps, R)
-    g_full = graph_of(R) if full else None
-    g_rem = graph_of(rem) if rem else None
-    for gr in (g_full, g_rem):
-        if gr is not None:
-            gr.replay()
-    torch.cuda.synchronize()
+    if args.eager:  # counter collection: plain launches, no graph
+        ms_total = timed(lambda: [step(i % R) for i in range(steps)], 1, stream)
+    else:
+        full, rem = divmod(steps, R)
+        g_full = graph_of(R) if full else None
+        g_rem = graph_of(rem) if rem else None
+        for gr in (g_full, g_rem):
+            if gr is not None:
+                gr.replay()
+        torch.cuda.synchronize()
 
-    def run_steps():
-        for _ in range(full):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
+        def run_steps():
+            for _ in range(full):
+                g_full.replay()
+            if g_rem is not None:
+                g_rem.replay()
 
-    ms_total = timed(run_steps, 1, stream)
+        ms_total = timed(run_steps, 1, stream)
     ms_step = ms_total / steps
     # the step is one kernel: its average duration is the step time of
     # back-to-back graph launches (an upper bound: it includes launch gaps)
@@ -160,9 +203,11 @@ def gemv_leg(args, steps, warmup):
         config={"workload": "gemv_4096" if not args.rows else f"gemv_4096_rows{N}", "M": 1,
                 "K": K, "N": N, "x_dtype": "bf16", "w_dtype": "fp32 (packed offline)",
                 "epilogue": "alpha-scaled fp32", "weight_ring": R,
-                "bytes_per_step": bytes_step, "hip_graph": True},
+                "bytes_per_step": bytes_step, "hip_graph": not args.eager},
         roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                  "frac": achieved / HBM_PEAK_GBS,
+                  "traffic": recorded_traffic("gemv_4096_traffic.md", GEMV_SOURCES)
+                  if not args.rows else None,
                   "kernel": "gemv_kernel (bf16 activations packed in-kernel, alpha-scaled)",
                   "kernel_avg_us": ms_gemv * 1e3,
                   "algorithmic_bytes_per_launch": bytes_gemv},
@@ -205,7 +250,8 @@ def ffn_leg(steps, warmup):
                 "w_dtype": "fp32 (packed offline)", "epilogue": "alpha-scaled fp32"},
         roofline={"bound": "mfma", "achieved": ach / 1e12, "peak": MFMA_FP4_PEAK_OPS / 1e12,
                   "unit": "T binary-ops/s (= FP4 TFLOP/s)", "frac": ach / MFMA_FP4_PEAK_OPS,
-                  "traffic": None, "kernel": "gemm_mfma_kernel (alpha-scaled)",
+                  "traffic": recorded_traffic("ffn_4096_traffic.md", MFMA_SOURCES),
+                  "kernel": "gemm_mfma_kernel (alpha-scaled)",
                   "kernel_avg_us": ms_gemm * 1e3, "algorithmic_ops_per_launch": ops,
                   "frac_of_valu_popcount_peak": ach / ALU_PEAK_BINARY_OPS},
         ablation={"valu_xor_popcount_us": ms_valu * 1e3, "mfma_fp4_us": ms_gemm * 1e3,
@@ -335,6 +381,15 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import packed_xor_popcount_amd as bnn
     bnn.library()  # fail loudly if the HIP library is missing
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.calibrate_copy} MiB x 8")
+        return
 
     defaults = {"gemv_4096": (1024, 64), "ffn_4096": (20, 3), "chain_65536": (50, 5)}
     steps = args.steps if args.steps is not None else defaults[args.workload][0]
