@@ -45,6 +45,12 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // Wave arrangement and per-wave tiles of the wide-output configuration.
+#ifndef BNN_MFMA_SW
+#define BNN_MFMA_SW 8  // words of K per register step
+#endif
+#ifndef BNN_MFMA_SCHED
+#define BNN_MFMA_SCHED 0  // VALU ops to interleave after each MFMA (0: compiler's choice)
+#endif
 #ifndef BNN_MFMA_WR
 #define BNN_MFMA_WR 4
 #define BNN_MFMA_WC 1
@@ -154,7 +160,7 @@ __global__ void __launch_bounds__(256)
   // q (0..7) pairs half (q & 1) of word (q >> 1) of both lane halves.  A step
   // is "clean" when all its elements are inside K; only the last step can
   // be partial.
-  constexpr int kSW = 8, kHW = kSW / 2;
+  constexpr int kSW = BNN_MFMA_SW, kHW = kSW / 2;
   const int nsteps = (kw + kSW - 1) / kSW;
   const int nclean = (K >> 6) / kSW;
 
@@ -199,6 +205,14 @@ __global__ void __launch_bounds__(256)
             acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 ao[q][rb], bo[q][cb], acc[rb][cb], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
     }
+#if BNN_MFMA_SCHED
+    // Interleave: one MFMA, then a few VALU ops (the next word's unpack).
+#pragma unroll
+    for (int j = 0; j < kHW * 2 * RB * CB; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, BNN_MFMA_SCHED, 0);
+    }
+#endif
   };
 
   // Two register buffers in ping-pong: the loads of step s+1 are in flight

@@ -40,6 +40,9 @@ constexpr int kChunkWords = 512;  // fused packer: K-chunk held in LDS per row
 #ifndef BNN_GEMV_BLOCKS_PER_CU
 #define BNN_GEMV_BLOCKS_PER_CU 8
 #endif
+#ifndef BNN_GEMV_SMALL_P
+#define BNN_GEMV_SMALL_P 1
+#endif
 constexpr int kBlocksPerCU = BNN_GEMV_BLOCKS_PER_CU;  // persistent grid size (x 256 CUs)
 
 template <int EPI, int L, int VEC, int P, int XT>
@@ -294,19 +297,28 @@ __global__ void __launch_bounds__(256)
   // Every activation row holds whole 16-byte-aligned groups of 8 elements
   // (the launcher checks this), so the loads are unconditional vector loads;
   // slots past the last word re-read the last one and are not stored.
+  // Rounds s past the last word are skipped (uniform branches); with a
+  // single row the word index needs no division.
   auto x_round = [&](int q0, Raw8(&raw)[kS]) {
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
+      if (q0 + s * 32 >= total) break;
       int q = q0 + s * 32 + grp;
       q = q < total ? q : total - 1;
-      const int r = q / kw, wd = q - r * kw;
-      const int64_t e0 = (int64_t)r * ldx + (int64_t)wd * 64 + 8 * t8;
+      int64_t e0;
+      if (M == 1) {
+        e0 = (int64_t)q * 64 + 8 * t8;
+      } else {
+        const int r = q / kw, wd = q - r * kw;
+        e0 = (int64_t)r * ldx + (int64_t)wd * 64 + 8 * t8;
+      }
       raw[s] = load_raw8<DT, true>(xv, e0, 8);
     }
   };
   auto x_store = [&](int q0, const Raw8(&raw)[kS]) {
 #pragma unroll
     for (int s = 0; s < kS; ++s) {
+      if (q0 + s * 32 >= total) break;
       const int q = q0 + s * 32 + grp;
       const uint64_t word = word_from_bytes(byte_of<DT>(raw[s]), t8);
       if (t8 == 0 && q < total) xs[q] = word;  // row r, word w at r * kw + w == q
@@ -316,6 +328,19 @@ __global__ void __launch_bounds__(256)
   bool first = true;
   for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
     const int64_t nb = (int64_t)step * CB;
+    // Scales of the columns this lane will store (int32 / scaled epilogues
+    // store from the reducing lanes), issued first: their latency then
+    // overlaps the W and activation loads instead of following the pack.
+    float a_pre[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      a_pre[p] = 0.0f;
+      if (EPI == BNN_EPI_SCALED) {
+        int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+        n = n < N ? n : N - 1;
+        a_pre[p] = alpha[n];
+      }
+    }
     uint64_t w[P][VEC];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -340,18 +365,6 @@ __global__ void __launch_bounds__(256)
       }
       __syncthreads();
       first = false;
-    }
-    // Scales of the columns this lane will store (int32 / scaled epilogues
-    // store from the reducing lanes directly).
-    float a_pre[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      a_pre[p] = 0.0f;
-      if (EPI == BNN_EPI_SCALED) {
-        int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
-        n = n < N ? n : N - 1;
-        a_pre[p] = alpha[n];
-      }
     }
 
     uint32_t acc[P][kMR];
@@ -468,7 +481,7 @@ hipError_t launch_l(const Args &a, hipStream_t s) {
     // keeps four W loads in flight per step when streaming large W.
     constexpr int CB1 = 4 * (64 / L);
     if ((int64_t)a.N <= (int64_t)CB1 * 256 * kBlocksPerCU)
-      return launch_lp<EPI, L, VEC, XT, 1>(a, s);
+      return launch_lp<EPI, L, VEC, XT, BNN_GEMV_SMALL_P>(a, s);
     return launch_lp<EPI, L, VEC, XT, 4>(a, s);
   }
 }

@@ -65,17 +65,48 @@ __device__ __forceinline__ Raw8 load_raw8(const void *src, int64_t e0, int n_ok)
   return r;
 }
 
-// Sign byte of 8 loaded elements: element e -> bit e (1 when it projects to -1).
+// Sign byte of 8 loaded elements: element e -> bit e (1 when it projects to
+// -1), from packed arithmetic instead of one compare per element:
+//  * bf16 (two per dword): t = h - 1 (wrapping), u = t + 0x80 saturating at
+//    0xFFFF, both as packed 16-bit ops; u >= 0x8000 exactly when
+//    t >= 0x7F80, i.e. when the value is not > 0.  So the projection bit of
+//    each element is the most significant bit of its half.
+//  * fp32: the same with t = b - 1, u = t + 0x00800000 saturating at
+//    0xFFFFFFFF: the bit is the most significant bit of u.
+// v_perm_b32 then gathers the four bytes that carry those bits into one
+// dword, and a multiply collects the four bits (bit 7, 15, 23, 31) into the
+// low nibble: ((x & 0x80808080) >> 7) * 0x00204081 puts them at bits 21..24
+// with no carries in between.
+typedef unsigned short bnn_u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t msb_nibble(uint32_t x) {
+  const uint32_t t = (x & 0x80808080u) >> 7;
+  return ((t * 0x00204081u) >> 21) & 0xFu;
+}
+
+__device__ __forceinline__ uint32_t bf16_pair_minus(uint32_t d) {
+  const bnn_u16x2 h = __builtin_bit_cast(bnn_u16x2, d);
+  const bnn_u16x2 one = {1, 1}, bias = {0x80, 0x80};
+  const bnn_u16x2 u = __builtin_elementwise_add_sat(h - one, bias);
+  return __builtin_bit_cast(uint32_t, u);  // bits 15 and 31
+}
+
+__device__ __forceinline__ uint32_t f32_minus(uint32_t b) {
+  return __builtin_elementwise_add_sat(b - 1u, 0x00800000u);  // bit 31
+}
+
 template <int DT>
 __device__ __forceinline__ uint32_t byte_of(const Raw8 &r) {
-  if (DT == 0)
-    return minus_f32(r.a.x) | minus_f32(r.a.y) << 1 | minus_f32(r.a.z) << 2 |
-           minus_f32(r.a.w) << 3 | minus_f32(r.b.x) << 4 | minus_f32(r.b.y) << 5 |
-           minus_f32(r.b.z) << 6 | minus_f32(r.b.w) << 7;
-  return minus_bf16(r.a.x & 0xFFFFu) | minus_bf16(r.a.x >> 16) << 1 |
-         minus_bf16(r.a.y & 0xFFFFu) << 2 | minus_bf16(r.a.y >> 16) << 3 |
-         minus_bf16(r.a.z & 0xFFFFu) << 4 | minus_bf16(r.a.z >> 16) << 5 |
-         minus_bf16(r.a.w & 0xFFFFu) << 6 | minus_bf16(r.a.w >> 16) << 7;
+  if (DT == 0) {
+    const uint32_t lo = __builtin_amdgcn_perm(f32_minus(r.a.y), f32_minus(r.a.x), 0x0C0C0703u) |
+                        __builtin_amdgcn_perm(f32_minus(r.a.w), f32_minus(r.a.z), 0x07030C0Cu);
+    const uint32_t hi = __builtin_amdgcn_perm(f32_minus(r.b.y), f32_minus(r.b.x), 0x0C0C0703u) |
+                        __builtin_amdgcn_perm(f32_minus(r.b.w), f32_minus(r.b.z), 0x07030C0Cu);
+    return msb_nibble(lo) | (msb_nibble(hi) << 4);
+  }
+  const uint32_t lo = __builtin_amdgcn_perm(bf16_pair_minus(r.a.y), bf16_pair_minus(r.a.x), 0x07050301u);
+  const uint32_t hi = __builtin_amdgcn_perm(bf16_pair_minus(r.a.w), bf16_pair_minus(r.a.z), 0x07050301u);
+  return msb_nibble(lo) | (msb_nibble(hi) << 4);
 }
 
 // Assemble the bytes of 8 consecutive lanes (lane & 7 == t holds the byte for
