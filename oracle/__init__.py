@@ -70,8 +70,10 @@ def _load():
     lib.oracle_gemm_scaled.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_int]
     lib.oracle_sign_repack.argtypes = [P, P, I64, I64, I64, P, ctypes.c_int]
     lib.oracle_dot_pairs.argtypes = [P, P, I64, P, P, I64, P]
+    lib.oracle_sign_repack_thr.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_int]
     for name in ("oracle_pack_f32", "oracle_pack_bf16", "oracle_unpack", "oracle_gemm_i32",
-                 "oracle_gemm_scaled", "oracle_sign_repack", "oracle_dot_pairs"):
+                 "oracle_gemm_scaled", "oracle_sign_repack", "oracle_dot_pairs",
+                 "oracle_sign_repack_thr"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -171,6 +173,26 @@ def sign_repack(xp: np.ndarray, wp: np.ndarray, k: int, nthreads: int = 0) -> np
     y = np.zeros((M, words(N)), dtype=np.uint64)
     if M and N:
         _load().oracle_sign_repack(_ptr(xp), _ptr(wp), M, N, k, _ptr(y), nthreads)
+    return y
+
+
+def sign_repack_thr(xp: np.ndarray, wp: np.ndarray, thr: np.ndarray, k: int, flip=None,
+                    nthreads: int = 0) -> np.ndarray:
+    """uint64 ``(M, words(N))``: bit n of row m is 1 when ``<x_m, w_n> <= thr[n]``,
+    inverted where ``flip[n]`` is non-zero (the folded form of a BatchNorm
+    between binary layers)."""
+    xp, wp = _check_packed(xp, wp, k)
+    M, N = xp.shape[0], wp.shape[0]
+    thr = np.ascontiguousarray(thr, dtype=np.int32)
+    if thr.shape != (N,):
+        raise ValueError("thr must have one value per output channel")
+    fl = None if flip is None else np.ascontiguousarray(flip, dtype=np.uint8)
+    if fl is not None and fl.shape != (N,):
+        raise ValueError("flip must have one value per output channel")
+    y = np.zeros((M, words(N)), dtype=np.uint64)
+    if M and N:
+        _load().oracle_sign_repack_thr(_ptr(xp), _ptr(wp), _ptr(thr),
+                                       None if fl is None else _ptr(fl), M, N, k, _ptr(y), nthreads)
     return y
 
 

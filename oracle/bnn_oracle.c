@@ -33,6 +33,9 @@
  *     packed along N with the same bit order; pad bits are 0 (+1).
  *   - scaled output: one fp32 multiply, (float)dot * alpha[n], rounded to
  *     nearest even.
+ *   - threshold repack ("Architecture Decision Record", Decision: "BN after
+ *     binary"): a BatchNorm followed by the next layer's projection reduces
+ *     to "-1 when dot <= t[n]", inverted on channels with a negative scale.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared -pthread
  *        bnn_oracle.c -o libbnn_oracle.so
@@ -114,12 +117,14 @@ static int64_t dot_pm1(const int8_t *a, const int8_t *b, int64_t k) {
 /* Row-parallel driver: rows of X are split over threads; integer sums make
  * the result independent of the split. */
 
-enum { OUT_I32 = 0, OUT_SCALED = 1, OUT_REPACK = 2 };
+enum { OUT_I32 = 0, OUT_SCALED = 1, OUT_REPACK = 2, OUT_REPACK_THR = 3 };
 
 typedef struct {
   const uint64_t *xp;
   const int8_t *wu; /* W unpacked once: N x K */
   const float *alpha;
+  const int32_t *thr;   /* OUT_REPACK_THR: per-channel threshold */
+  const uint8_t *flip;  /* OUT_REPACK_THR: per-channel flip, or NULL */
   void *y;
   int64_t m_begin, m_end, N, K;
   int mode;
@@ -140,6 +145,19 @@ static void *gemm_rows(void *arg) {
         /* [BME 1] projection applied to the integer output: <= 0 -> -1. */
         int s = (d > 0) ? 1 : -1;
         yp[n / 64] |= bit_of_sign(s) << (n % 64);
+      }
+    } else if (j->mode == OUT_REPACK_THR) {
+      /* "Architecture Decision Record", Decision, "BN after binary": the next
+       * layer's input bit is the projection of a per-channel affine function
+       * of the dot, which reduces to "-1 when d <= t[n]", inverted when f[n]
+       * is set. */
+      uint64_t *yp = (uint64_t *)j->y + m * nw;
+      for (int64_t w = 0; w < nw; ++w) yp[w] = 0;
+      for (int64_t n = 0; n < j->N; ++n) {
+        int64_t d = dot_pm1(xu, j->wu + n * j->K, j->K);
+        int minus = d <= (int64_t)j->thr[n];
+        if (j->flip && j->flip[n]) minus = !minus;
+        yp[n / 64] |= (uint64_t)minus << (n % 64);
       }
     } else {
       for (int64_t n = 0; n < j->N; ++n) {
@@ -169,8 +187,9 @@ static int resolve_threads(int nthreads, int64_t M) {
   return nthreads;
 }
 
-static void run(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int64_t M,
-                int64_t N, int64_t K, int mode, int nthreads) {
+static void run(const uint64_t *xp, const uint64_t *wp, const float *alpha, const int32_t *thr,
+                const uint8_t *flip, void *y, int64_t M, int64_t N, int64_t K, int mode,
+                int nthreads) {
   if (M <= 0 || N <= 0) return;
   int64_t kk = K > 0 ? K : 0;
   int8_t *wu = (int8_t *)malloc((size_t)(N * kk > 0 ? N * kk : 1));
@@ -182,6 +201,8 @@ static void run(const uint64_t *xp, const uint64_t *wp, const float *alpha, void
     jobs[t].xp = xp;
     jobs[t].wu = wu;
     jobs[t].alpha = alpha;
+    jobs[t].thr = thr;
+    jobs[t].flip = flip;
     jobs[t].y = y;
     jobs[t].m_begin = M * t / nt;
     jobs[t].m_end = M * (t + 1) / nt;
@@ -199,19 +220,29 @@ static void run(const uint64_t *xp, const uint64_t *wp, const float *alpha, void
  * W is N x words(K) (rows are output channels), Y is M x N row-major. */
 void oracle_gemm_i32(const uint64_t *xp, const uint64_t *wp, int64_t M, int64_t N, int64_t K,
                      int32_t *y, int nthreads) {
-  run(xp, wp, NULL, y, M, N, K, OUT_I32, nthreads);
+  run(xp, wp, NULL, NULL, NULL, y, M, N, K, OUT_I32, nthreads);
 }
 
 /* Y[m][n] = (float)<x_m, w_n> * alpha[n]  ([BME 1], channel scale). */
 void oracle_gemm_scaled(const uint64_t *xp, const uint64_t *wp, const float *alpha, int64_t M,
                         int64_t N, int64_t K, float *y, int nthreads) {
-  run(xp, wp, alpha, y, M, N, K, OUT_SCALED, nthreads);
+  run(xp, wp, alpha, NULL, NULL, y, M, N, K, OUT_SCALED, nthreads);
 }
 
 /* Packed M x words(N): bit n of row m is the projected sign of <x_m, w_n>. */
 void oracle_sign_repack(const uint64_t *xp, const uint64_t *wp, int64_t M, int64_t N, int64_t K,
                         uint64_t *yp, int nthreads) {
-  run(xp, wp, NULL, yp, M, N, K, OUT_REPACK, nthreads);
+  run(xp, wp, NULL, NULL, NULL, yp, M, N, K, OUT_REPACK, nthreads);
+}
+
+/* Packed M x words(N): bit n of row m is 1 when <x_m, w_n> <= thr[n], inverted
+ * where flip[n] is non-zero (flip may be NULL).  A BatchNorm between binary
+ * layers ("BN after binary", Architecture Decision Record) folds into
+ * (thr, flip); thr = 0 with no flips is oracle_sign_repack. */
+void oracle_sign_repack_thr(const uint64_t *xp, const uint64_t *wp, const int32_t *thr,
+                            const uint8_t *flip, int64_t M, int64_t N, int64_t K, uint64_t *yp,
+                            int nthreads) {
+  run(xp, wp, NULL, thr, flip, yp, M, N, K, OUT_REPACK_THR, nthreads);
 }
 
 /* out[i] = <x_{mi[i]}, w_{ni[i]}> for a list of (m, n) pairs: the sampled

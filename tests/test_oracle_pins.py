@@ -355,7 +355,7 @@ def test_threads_do_not_change_results():
 def _mutant(**over):
     ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in (
         "words", "pack", "unpack", "gemm_i32", "gemm_scaled", "sign_repack", "dot_pairs",
-        "chain", "sign_f32", "sign_bf16")})
+        "chain", "sign_f32", "sign_bf16", "sign_repack_thr")})
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -412,3 +412,46 @@ def test_pins_catch_planted_mistake(name, mut):
         except (AssertionError, ValueError, IndexError):
             failures += 1
     assert failures > 0, f"no pin catches the planted mistake: {name}"
+
+
+# --------------------------------------------------------------------------
+# Threshold repack ("Architecture Decision Record", Decision: "BN after
+# binary"): bit = (dot <= thr[n]) xor flip[n].
+
+
+def pin_repack_thr(o, seed=21):
+    rng = np.random.default_rng(seed)
+    for M, N, K in ((3, 70, 100), (5, 64, 65), (2, 130, 1000), (4, 1, 7)):
+        xp, wp = rand_packed(rng, M, K), rand_packed(rng, N, K)
+        # reduces to the plain projection rule at thr = 0, no flips
+        assert np.array_equal(o.sign_repack_thr(xp, wp, np.zeros(N, np.int32), K),
+                              o.sign_repack(xp, wp, K))
+        # brute force against numpy dots of independently unpacked operands
+        d = np_unpack(xp, K) @ np_unpack(wp, K).T
+        thr = rng.integers(-K - 2, K + 2, N).astype(np.int32)
+        flip = rng.integers(0, 2, N).astype(np.uint8)
+        bits = (d <= thr[None, :]) ^ (flip[None, :] == 1)
+        ref = o.pack(np.where(bits, -1.0, 1.0).astype(np.float32))
+        assert np.array_equal(o.sign_repack_thr(xp, wp, thr, K, flip), ref)
+        # extremes: every dot is in [-K, K]
+        allm = o.sign_repack_thr(xp, wp, np.full(N, K, np.int32), K)
+        assert np.array_equal(allm, o.pack(-np.ones((M, N), np.float32)))
+        none = o.sign_repack_thr(xp, wp, np.full(N, -K - 1, np.int32), K)
+        assert not none.any()
+
+
+def test_repack_thr():
+    pin_repack_thr(oracle)
+
+
+def test_pins_catch_threshold_mistakes():
+    o = oracle
+    bad = [
+        _mutant(sign_repack_thr=lambda xp, wp, t, k, flip=None, nthreads=0:
+                o.sign_repack_thr(xp, wp, np.asarray(t, np.int32) - 1, k, flip)),   # "<" for "<="
+        _mutant(sign_repack_thr=lambda xp, wp, t, k, flip=None, nthreads=0:
+                o.sign_repack_thr(xp, wp, t, k, None)),                            # flip ignored
+    ]
+    for m in bad:
+        with pytest.raises(AssertionError):
+            pin_repack_thr(m)
