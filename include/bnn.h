@@ -173,6 +173,32 @@ bnn_status bnn_gemm_sign_repack(const uint64_t *xp, const uint64_t *wp, uint64_t
                                 int64_t N, int64_t K, void *stream);
 
 /*
+ * bnn_gemm_sign_repack_thr -- sign -> repack against a per-output-channel
+ * integer threshold, with an optional per-channel flip: bit n of output row
+ * m is 1 (-1) when (K - 2d) <= thr[n], inverted where bit n of `flip` is 1.
+ * This is the form a BatchNorm placed after a binary layer takes when it is
+ * folded into the projection that feeds the next binary layer
+ * ("Architecture Decision Record", Decision: BN after the binary layers):
+ * with z = g*(a*dot - mu)/s + b, a positive slope g*a/s projects to -1
+ * exactly when dot <= floor(tau), tau = (mu - b*s/g)/a, and a negative slope
+ * exactly when not (dot <= ceil(tau) - 1), which is the flipped form.
+ * thr = 0 with no flip is bnn_gemm_sign_repack.
+ *
+ *   thr   N int32 thresholds, 4-byte aligned (any value; those >= K make
+ *         every dot pass, those < -K none).
+ *   flip  bnn_words(N) uint64 flip mask, bit n of word n/64 for channel n
+ *         (the bnn_pack_signs layout of a length-N row), 8-byte aligned, or
+ *         NULL for no flips.  Bits past N are ignored.
+ *   yp    M x bnn_words(N) uint64 output, 8-byte aligned; pad bits are 0.
+ *   algo  a BNN_ALGO_* value, as for bnn_gemm_ex (all bit-identical).
+ * Errors as bnn_gemm_u64, plus BNN_E_NULL for a NULL thr with M*N > 0 and
+ * BNN_E_ARG for an unknown algo.
+ */
+bnn_status bnn_gemm_sign_repack_thr(const uint64_t *xp, const uint64_t *wp, const int32_t *thr,
+                                    const uint64_t *flip, uint64_t *yp, int64_t M, int64_t N,
+                                    int64_t K, int algo, void *stream);
+
+/*
  * bnn_gemm_ex -- the general form of the three products above, with an
  * explicit kernel family (see bnn_algo; the matrix-core family takes the
  * same exact integer sum of +-1 products on the MFMA units, which "Binary

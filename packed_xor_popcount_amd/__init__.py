@@ -27,7 +27,7 @@ __all__ = [
     "BnnError", "EPI_I32", "EPI_SCALED", "EPI_REPACK", "ALGO_AUTO", "ALGO_GEMV", "ALGO_TILED",
     "ALGO_MFMA",
     "library", "library_path", "words", "pack_signs", "gemm_u64", "gemm_u64_scaled",
-    "gemm_sign_repack", "gemm_ex", "gemv_act", "version",
+    "gemm_sign_repack", "gemm_sign_repack_thr", "flip_words", "gemm_ex", "gemv_act", "version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +38,8 @@ EPI_I32, EPI_SCALED, EPI_REPACK = 0, 1, 2
 ALGO_AUTO, ALGO_GEMV, ALGO_TILED, ALGO_MFMA = 0, 1, 2, 3
 
 EXPORTED = ("bnn_words", "bnn_status_str", "bnn_version", "bnn_pack_signs", "bnn_gemm_u64",
-            "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex", "bnn_gemv_act")
+            "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex", "bnn_gemv_act",
+            "bnn_gemm_sign_repack_thr")
 
 
 class BnnError(RuntimeError):
@@ -71,8 +72,9 @@ def library():
     lib.bnn_gemm_sign_repack.argtypes = [P, P, P, I64, I64, I64, P]
     lib.bnn_gemm_ex.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
     lib.bnn_gemv_act.argtypes = [P, I, I64, P, P, P, I64, I64, I64, I, P]
+    lib.bnn_gemm_sign_repack_thr.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     for name in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack",
-                 "bnn_gemm_ex", "bnn_gemv_act"):
+                 "bnn_gemm_ex", "bnn_gemv_act", "bnn_gemm_sign_repack_thr"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -224,3 +226,40 @@ def gemm_u64_scaled(xp, wp, alpha, K, out=None):
 def gemm_sign_repack(xp, wp, K, out=None):
     """int64 ``(M, words(N))``: projected signs of ``<x_m, w_n>`` packed along N."""
     return gemm_ex(xp, wp, K, EPI_REPACK, ALGO_AUTO, None, out)
+
+
+def gemm_sign_repack_thr(xp, wp, thr, K, flip=None, algo=ALGO_AUTO, out=None):
+    """int64 ``(M, words(N))``: bit n of row m is 1 when ``<x_m, w_n> <= thr[n]``,
+    inverted where bit n of the packed ``flip`` mask is 1
+    (bnn_gemm_sign_repack_thr; the folded form of a BatchNorm after a binary
+    layer, see ``fold.bn_fold``).  ``thr`` is a contiguous int32 CUDA tensor
+    ``(N,)``; ``flip`` is None or a contiguous int64 CUDA tensor
+    ``(words(N),)`` (``flip_words`` builds one from per-channel flags)."""
+    M = _packed("xp", xp, K)
+    N = _packed("wp", wp, K)
+    if wp.device != xp.device:
+        raise ValueError("xp and wp must be on the same device")
+    _need_cuda("thr", thr)
+    if thr.dtype != torch.int32 or tuple(thr.shape) != (N,) or not thr.is_contiguous():
+        raise ValueError("thr must be a contiguous int32 tensor of shape (N,)")
+    if flip is not None:
+        _need_cuda("flip", flip)
+        if (flip.dtype != torch.int64 or tuple(flip.shape) != (words(N),)
+                or not flip.is_contiguous()):
+            raise ValueError("flip must be a contiguous int64 tensor of shape (words(N),)")
+    out = _out_for(EPI_REPACK, M, N, xp.device, out)
+    st = library().bnn_gemm_sign_repack_thr(_ptr(xp), _ptr(wp), _ptr(thr), _ptr(flip), _ptr(out),
+                                            M, N, int(K), int(algo), _stream(xp))
+    _check(st, "bnn_gemm_sign_repack_thr")
+    return out
+
+
+def flip_words(flags: torch.Tensor) -> torch.Tensor:
+    """Packed flip mask ``(words(N),)`` from N per-channel flags on a CUDA
+    device (non-zero = flip), packed by the library's sign packer: a flag
+    maps to -1 (bit 1), no flag to +1 (bit 0)."""
+    _need_cuda("flags", flags)
+    if flags.dim() != 1:
+        raise ValueError("flags must be 1-D")
+    signs = torch.where(flags != 0, -1.0, 1.0).to(torch.float32).reshape(1, -1)
+    return pack_signs(signs)[0]

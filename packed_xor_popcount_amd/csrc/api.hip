@@ -14,19 +14,43 @@ bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p) % a != 0; }
 
 bnn_status launch_status(hipError_t e) { return e == hipSuccess ? BNN_OK : BNN_E_LAUNCH; }
 
-bnn_status check_gemm(const uint64_t *xp, const uint64_t *wp, const float *alpha, const void *y,
-                      int64_t M, int64_t N, int64_t K, int epilogue, int algo) {
-  if (epilogue < BNN_EPI_I32 || epilogue > BNN_EPI_REPACK) return BNN_E_ARG;
+// Shared checks of the packed products; `epilogue` may be the internal
+// threshold repack, whose operands `ep.thr` / `ep.flip` are checked here too.
+bnn_status check_gemm(const uint64_t *xp, const uint64_t *wp, const bnn::EpiParams &ep,
+                      const void *y, int64_t M, int64_t N, int64_t K, int epilogue, int algo) {
+  if (epilogue < BNN_EPI_I32 || epilogue > bnn::kEpiRepackThr) return BNN_E_ARG;
   if (algo < BNN_ALGO_AUTO || algo > BNN_ALGO_MFMA) return BNN_E_ARG;
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return BNN_E_SHAPE;
   if (algo == BNN_ALGO_MFMA && K > bnn::kMfmaMaxK) return BNN_E_SHAPE;
   const int64_t kw = bnn_words(K);
   if ((M * kw > 0 && !xp) || (N * kw > 0 && !wp) || (M * N > 0 && !y)) return BNN_E_NULL;
-  if (epilogue == BNN_EPI_SCALED && M * N > 0 && !alpha) return BNN_E_NULL;
+  if (epilogue == BNN_EPI_SCALED && M * N > 0 && !ep.alpha) return BNN_E_NULL;
+  if (epilogue == bnn::kEpiRepackThr && M * N > 0 && !ep.thr) return BNN_E_NULL;
   if (misaligned(xp, 8) || misaligned(wp, 8)) return BNN_E_ALIGN;
-  if (misaligned(y, epilogue == BNN_EPI_REPACK ? 8 : 4)) return BNN_E_ALIGN;
-  if (epilogue == BNN_EPI_SCALED && misaligned(alpha, 4)) return BNN_E_ALIGN;
+  if (misaligned(y, bnn::is_repack(epilogue) ? 8 : 4)) return BNN_E_ALIGN;
+  if (epilogue == BNN_EPI_SCALED && misaligned(ep.alpha, 4)) return BNN_E_ALIGN;
+  if (epilogue == bnn::kEpiRepackThr && (misaligned(ep.thr, 4) || misaligned(ep.flip, 8)))
+    return BNN_E_ALIGN;
   return BNN_OK;
+}
+
+// Kernel choice and launch of a validated product.
+bnn_status run_gemm(const uint64_t *xp, const uint64_t *wp, const bnn::EpiParams &ep, void *y,
+                    int64_t M, int64_t N, int64_t K, int epilogue, int algo, hipStream_t s) {
+  if (M == 0 || N == 0) return BNN_OK;
+  if (algo == BNN_ALGO_AUTO) {
+    if (M <= kGemvMaxM)
+      algo = BNN_ALGO_GEMV;  // weight-streaming: HBM-bound
+    else if (K <= bnn::kMfmaMaxK)
+      algo = BNN_ALGO_MFMA;  // matrix cores: ~8x the VALU popcount rate
+    else
+      algo = BNN_ALGO_TILED;
+  }
+  if (algo == BNN_ALGO_GEMV)
+    return launch_status(bnn::launch_gemv(xp, wp, ep, y, M, N, K, epilogue, s));
+  if (algo == BNN_ALGO_MFMA)
+    return launch_status(bnn::launch_gemm_mfma(xp, wp, ep, y, M, N, K, epilogue, s));
+  return launch_status(bnn::launch_gemm_tiled(xp, wp, ep, y, M, N, K, epilogue, s));
 }
 
 }  // namespace
@@ -64,23 +88,21 @@ bnn_status bnn_pack_signs(const void *src, int dtype, int64_t rows, int64_t k, i
 
 bnn_status bnn_gemm_ex(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
                        int64_t M, int64_t N, int64_t K, int epilogue, int algo, void *stream) {
-  const bnn_status st = check_gemm(xp, wp, alpha, y, M, N, K, epilogue, algo);
+  if (epilogue < BNN_EPI_I32 || epilogue > BNN_EPI_REPACK) return BNN_E_ARG;
+  const bnn::EpiParams ep{alpha, nullptr, nullptr};
+  const bnn_status st = check_gemm(xp, wp, ep, y, M, N, K, epilogue, algo);
   if (st != BNN_OK) return st;
-  if (M == 0 || N == 0) return BNN_OK;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (algo == BNN_ALGO_AUTO) {
-    if (M <= kGemvMaxM)
-      algo = BNN_ALGO_GEMV;  // weight-streaming: HBM-bound
-    else if (K <= bnn::kMfmaMaxK)
-      algo = BNN_ALGO_MFMA;  // matrix cores: ~8x the VALU popcount rate
-    else
-      algo = BNN_ALGO_TILED;
-  }
-  if (algo == BNN_ALGO_GEMV)
-    return launch_status(bnn::launch_gemv(xp, wp, alpha, y, M, N, K, epilogue, s));
-  if (algo == BNN_ALGO_MFMA)
-    return launch_status(bnn::launch_gemm_mfma(xp, wp, alpha, y, M, N, K, epilogue, s));
-  return launch_status(bnn::launch_gemm_tiled(xp, wp, alpha, y, M, N, K, epilogue, s));
+  return run_gemm(xp, wp, ep, y, M, N, K, epilogue, algo, static_cast<hipStream_t>(stream));
+}
+
+bnn_status bnn_gemm_sign_repack_thr(const uint64_t *xp, const uint64_t *wp, const int32_t *thr,
+                                    const uint64_t *flip, uint64_t *yp, int64_t M, int64_t N,
+                                    int64_t K, int algo, void *stream) {
+  const bnn::EpiParams ep{nullptr, thr, flip};
+  const bnn_status st = check_gemm(xp, wp, ep, yp, M, N, K, bnn::kEpiRepackThr, algo);
+  if (st != BNN_OK) return st;
+  return run_gemm(xp, wp, ep, yp, M, N, K, bnn::kEpiRepackThr, algo,
+                  static_cast<hipStream_t>(stream));
 }
 
 bnn_status bnn_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
@@ -98,7 +120,8 @@ bnn_status bnn_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *w
   if (misaligned(y, epilogue == BNN_EPI_REPACK ? 8 : 4)) return BNN_E_ALIGN;
   if (epilogue == BNN_EPI_SCALED && misaligned(alpha, 4)) return BNN_E_ALIGN;
   if (M == 0 || N == 0) return BNN_OK;
-  return launch_status(bnn::launch_gemv_act(x, dtype, ldx, wp, alpha, y, M, N, K, epilogue,
+  const bnn::EpiParams ep{alpha, nullptr, nullptr};
+  return launch_status(bnn::launch_gemv_act(x, dtype, ldx, wp, ep, y, M, N, K, epilogue,
                                             static_cast<hipStream_t>(stream)));
 }
 

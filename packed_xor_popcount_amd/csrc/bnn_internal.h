@@ -5,33 +5,62 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/bnn.h"
+
 namespace bnn {
+
+// Mask of the logical bits of a row's last 64-bit word.
+__host__ __device__ inline uint64_t tail_mask(int64_t k) {
+  const int r = (int)(k & 63);
+  return r ? ((uint64_t(1) << r) - 1) : ~uint64_t(0);
+}
+
+// Epilogue selector beyond the public ones: sign -> repack against a
+// per-channel threshold, with an optional flip mask (bnn_gemm_sign_repack_thr).
+constexpr int kEpiRepackThr = 3;
+__host__ __device__ constexpr bool is_repack(int epi) {
+  return epi == BNN_EPI_REPACK || epi == kEpiRepackThr;
+}
+
+// Per-output-channel epilogue operands (each used by one epilogue only).
+struct EpiParams {
+  const float *alpha;    // [N] fp32 scales (BNN_EPI_SCALED)
+  const int32_t *thr;    // [N] thresholds (kEpiRepackThr)
+  const uint64_t *flip;  // [words(N)] flip mask or null (kEpiRepackThr)
+};
 
 // Launchers: each enqueues its kernel(s) on `s` and returns hipGetLastError().
 // Arguments are already validated by the C-ABI layer.
 hipError_t launch_pack(const void *src, int dtype, int64_t rows, int64_t k, int64_t ld,
                        uint64_t *dst, hipStream_t s);
 
-hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y,
                              int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
 
 // Matrix-core (FP4 MFMA) GEMM; exact while K <= 2^24.
-hipError_t launch_gemm_mfma(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+hipError_t launch_gemm_mfma(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y,
                             int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
 
-hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y,
                        int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s);
 
 // GEMV whose activation rows arrive as fp32 (dtype 0) or bf16 (dtype 1)
 // values, row stride ldx elements, and are sign-packed inside the kernel.
 hipError_t launch_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
-                           const float *alpha, void *y, int64_t M, int64_t N, int64_t K,
+                           const EpiParams &ep, void *y, int64_t M, int64_t N, int64_t K,
                            int epilogue, hipStream_t s);
 
-// Mask of the logical bits of a row's last 64-bit word.
-__host__ __device__ inline uint64_t tail_mask(int64_t k) {
-  const int r = (int)(k & 63);
-  return r ? ((uint64_t(1) << r) - 1) : ~uint64_t(0);
+// Threshold-repack operands, loaded by the kernels before their K loops from
+// clamped (always in-bounds) indexes: the threshold of output column n, and
+// the flip word of 64-column group wi with its bits past column N cleared
+// (so that pad bits of the output stay 0).
+__device__ __forceinline__ int32_t thr_of(const EpiParams &ep, int64_t n, int64_t N) {
+  return ep.thr[n < N ? n : N - 1];
+}
+__device__ __forceinline__ uint64_t flip_of(const EpiParams &ep, int64_t wi, int64_t N) {
+  if (!ep.flip) return 0;
+  const int64_t nw = (N + 63) >> 6;
+  return wi < nw - 1 ? ep.flip[wi] : (ep.flip[nw - 1] & tail_mask(N));
 }
 
 constexpr int kWave = 64;  // CDNA wavefront width

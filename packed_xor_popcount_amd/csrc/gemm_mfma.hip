@@ -111,10 +111,10 @@ __device__ __forceinline__ uint32_t valid_bits(int64_t e, int64_t K) {
 template <int EPI, int WR, int WC, int RB, int CB>
 __global__ void __launch_bounds__(256)
     gemm_mfma_kernel(const uint64_t *__restrict__ xp, const uint64_t *__restrict__ wp,
-                     const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
-                     int kw, int tiles_n) {
+                     const EpiParams ep, void *__restrict__ yv, int M, int N, int K, int kw,
+                     int tiles_n) {
   static_assert(WR * WC == 4, "4 waves per block");
-  static_assert(EPI != BNN_EPI_REPACK || CB % 2 == 0, "repack pairs 32-column tiles");
+  static_assert(!is_repack(EPI) || CB % 2 == 0, "repack pairs 32-column tiles");
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -141,12 +141,24 @@ __global__ void __launch_bounds__(256)
     bcol[cb] = wp + (int64_t)n * kw;
   }
 
+  // Per-column epilogue operands, fetched before the K loop: the scale, or
+  // the threshold as an fp32 bound that is exact against the (exact, |d| <=
+  // K <= 2^24) accumulators -- +inf / -inf outside [-K, K] -- and the flip
+  // word of each 64-column pair.
   float a_pre[CB];
+  uint64_t f_pre[CB / 2 > 0 ? CB / 2 : 1];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int n = n0 + cb * 32 + li;
-    a_pre[cb] = (EPI == BNN_EPI_SCALED && n < N) ? alpha[n] : 0.0f;
+    a_pre[cb] = (EPI == BNN_EPI_SCALED && n < N) ? ep.alpha[n] : 0.0f;
+    if (EPI == kEpiRepackThr) {
+      const int32_t t = thr_of(ep, n, N);
+      a_pre[cb] = t >= K ? __builtin_inff() : (t < -K ? -__builtin_inff() : (float)t);
+    }
   }
+#pragma unroll
+  for (int cp = 0; cp < CB / 2; ++cp)
+    f_pre[cp] = EPI == kEpiRepackThr ? flip_of(ep, (n0 >> 6) + cp, N) : 0;
   v16f acc[RB][CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -246,7 +258,7 @@ __global__ void __launch_bounds__(256)
 
   // Epilogue.  acc[rb][cb][v] is the exact integer dot of row
   // m0 + rb*32 + 8(v/4) + 4h + v%4 and column n0 + cb*32 + li.
-  if (EPI == BNN_EPI_REPACK) {
+  if (is_repack(EPI)) {
     const int nw = (N + 63) >> 6;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -256,13 +268,15 @@ __global__ void __launch_bounds__(256)
         const int wi = (n0 >> 6) + cp;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const uint64_t lo = __builtin_amdgcn_ballot_w64(na < N && acc[rb][2 * cp][v] <= 0.0f);
-          const uint64_t hi = __builtin_amdgcn_ballot_w64(nb2 < N && acc[rb][2 * cp + 1][v] <= 0.0f);
+          // bit set (-1) where the dot is <= the threshold (0 for the plain repack)
+          const uint64_t lo = __builtin_amdgcn_ballot_w64(na < N && acc[rb][2 * cp][v] <= a_pre[2 * cp]);
+          const uint64_t hi =
+              __builtin_amdgcn_ballot_w64(nb2 < N && acc[rb][2 * cp + 1][v] <= a_pre[2 * cp + 1]);
           const int r0 = m0 + rb * 32 + 8 * (v >> 2) + (v & 3);
           // lane 0 writes row r0, lane 32 writes row r0 + 4
           const int r = r0 + 4 * h;
-          const uint64_t word = h ? ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32))
-                                  : ((hi << 32) | (lo & 0xFFFFFFFFull));
+          const uint64_t word = (h ? ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32))
+                                   : ((hi << 32) | (lo & 0xFFFFFFFFull))) ^ f_pre[cp];
           if (li == 0 && r < M && wi < nw) static_cast<uint64_t *>(yv)[(int64_t)r * nw + wi] = word;
         }
       }
@@ -300,37 +314,39 @@ __global__ void __launch_bounds__(256)
 }
 
 template <int EPI, int WR, int WC, int RB, int CB>
-hipError_t launch_cfg(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
+hipError_t launch_cfg(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y, int M,
                       int N, int K, hipStream_t s) {
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
   const int kw = (K + 63) / 64;
   const int tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = (int64_t)((M + BM - 1) / BM) * tiles_n;
   hipLaunchKernelGGL((gemm_mfma_kernel<EPI, WR, WC, RB, CB>), dim3((unsigned)tiles), dim3(256), 0,
-                     s, xp, wp, alpha, y, M, N, K, kw, tiles_n);
+                     s, xp, wp, ep, y, M, N, K, kw, tiles_n);
   return hipGetLastError();
 }
 
 template <int EPI>
-hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y, int M,
+hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y, int M,
                       int N, int K, hipStream_t s) {
   // Narrow outputs stack the four waves along M so that no wave idles.
-  if (N <= 64) return launch_cfg<EPI, 4, 1, 1, 2>(xp, wp, alpha, y, M, N, K, s);  // 128 x 64
-  return launch_cfg<EPI, BNN_MFMA_WR, BNN_MFMA_WC, BNN_MFMA_RB, BNN_MFMA_CB>(xp, wp, alpha, y, M, N,
-                                                                          K, s);
+  if (N <= 64) return launch_cfg<EPI, 4, 1, 1, 2>(xp, wp, ep, y, M, N, K, s);  // 128 x 64
+  return launch_cfg<EPI, BNN_MFMA_WR, BNN_MFMA_WC, BNN_MFMA_RB, BNN_MFMA_CB>(xp, wp, ep, y, M, N, K,
+                                                                          s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_mfma(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+hipError_t launch_gemm_mfma(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y,
                             int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s) {
   switch (epilogue) {
     case BNN_EPI_I32:
-      return launch_epi<BNN_EPI_I32>(xp, wp, alpha, y, (int)M, (int)N, (int)K, s);
+      return launch_epi<BNN_EPI_I32>(xp, wp, ep, y, (int)M, (int)N, (int)K, s);
     case BNN_EPI_SCALED:
-      return launch_epi<BNN_EPI_SCALED>(xp, wp, alpha, y, (int)M, (int)N, (int)K, s);
+      return launch_epi<BNN_EPI_SCALED>(xp, wp, ep, y, (int)M, (int)N, (int)K, s);
+    case kEpiRepackThr:
+      return launch_epi<kEpiRepackThr>(xp, wp, ep, y, (int)M, (int)N, (int)K, s);
     default:
-      return launch_epi<BNN_EPI_REPACK>(xp, wp, alpha, y, (int)M, (int)N, (int)K, s);
+      return launch_epi<BNN_EPI_REPACK>(xp, wp, ep, y, (int)M, (int)N, (int)K, s);
   }
 }
 

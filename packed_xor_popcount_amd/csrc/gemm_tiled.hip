@@ -46,8 +46,8 @@ __device__ __forceinline__ uint64_t load_word(const uint64_t *__restrict__ p, in
 template <int EPI>
 __global__ void __launch_bounds__(256)
     gemm_tiled_kernel(const uint64_t *__restrict__ xp, const uint64_t *__restrict__ wp,
-                      const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
-                      int kw, int tiles_n, int64_t tiles) {
+                      const EpiParams ep, void *__restrict__ yv, int M, int N, int K, int kw,
+                      int tiles_n, int64_t tiles) {
   __shared__ __attribute__((aligned(16))) unsigned char wl[kBN * kLdsStride];
   __shared__ __attribute__((aligned(16))) uint64_t xl[kBM][kKC];
   const int tid = threadIdx.x;
@@ -60,14 +60,19 @@ __global__ void __launch_bounds__(256)
   const int n0 = tn * kBN;
   const uint64_t tmask = tail_mask(K);
 
-  // Scales of this lane's columns, fetched before the K loop (on gfx9 the
-  // vector-memory counter also counts stores, so a load between the
-  // epilogue's stores would make later waits drain them).
+  // Scales (or thresholds and flip words) of this lane's columns, fetched
+  // before the K loop (on gfx9 the vector-memory counter also counts stores,
+  // so a load between the epilogue's stores would make later waits drain
+  // them).
   float a_pre[kColsPerLane];
+  int32_t t_pre[kColsPerLane];
+  uint64_t f_pre[kColsPerLane];
 #pragma unroll
   for (int c = 0; c < kColsPerLane; ++c) {
     const int n = n0 + lane + 64 * c;
-    a_pre[c] = (EPI == BNN_EPI_SCALED && n < N) ? alpha[n] : 0.0f;
+    a_pre[c] = (EPI == BNN_EPI_SCALED && n < N) ? ep.alpha[n] : 0.0f;
+    t_pre[c] = EPI == kEpiRepackThr ? thr_of(ep, n, N) : 0;
+    f_pre[c] = EPI == kEpiRepackThr ? flip_of(ep, (n0 >> 6) + c, N) : 0;
   }
 
   uint32_t acc[kRowsPerWave][kColsPerLane];
@@ -144,7 +149,7 @@ __global__ void __launch_bounds__(256)
       } else if (EPI == BNN_EPI_SCALED) {
         if (n < N) static_cast<float *>(yv)[(int64_t)m * N + n] = __fmul_rn((float)dot, a);
       } else {
-        const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= 0);
+        const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= t_pre[c]) ^ f_pre[c];
         const int wi = (n0 >> 6) + c;
         if (lane == 0 && wi < nw) static_cast<uint64_t *>(yv)[(int64_t)m * nw + wi] = word;
       }
@@ -156,7 +161,7 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y,
                              int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s) {
   const int kw = (int)((K + 63) / 64);
   const int tiles_n = (int)((N + kBN - 1) / kBN);
@@ -165,15 +170,19 @@ hipError_t launch_gemm_tiled(const uint64_t *xp, const uint64_t *wp, const float
   const dim3 grid((unsigned)(tiles < cap ? tiles : cap)), block(256);
   switch (epilogue) {
     case BNN_EPI_I32:
-      hipLaunchKernelGGL(gemm_tiled_kernel<BNN_EPI_I32>, grid, block, 0, s, xp, wp, alpha, y,
-                         (int)M, (int)N, (int)K, kw, tiles_n, tiles);
+      hipLaunchKernelGGL(gemm_tiled_kernel<BNN_EPI_I32>, grid, block, 0, s, xp, wp, ep, y, (int)M,
+                         (int)N, (int)K, kw, tiles_n, tiles);
       break;
     case BNN_EPI_SCALED:
-      hipLaunchKernelGGL(gemm_tiled_kernel<BNN_EPI_SCALED>, grid, block, 0, s, xp, wp, alpha, y,
+      hipLaunchKernelGGL(gemm_tiled_kernel<BNN_EPI_SCALED>, grid, block, 0, s, xp, wp, ep, y,
+                         (int)M, (int)N, (int)K, kw, tiles_n, tiles);
+      break;
+    case kEpiRepackThr:
+      hipLaunchKernelGGL(gemm_tiled_kernel<kEpiRepackThr>, grid, block, 0, s, xp, wp, ep, y,
                          (int)M, (int)N, (int)K, kw, tiles_n, tiles);
       break;
     default:
-      hipLaunchKernelGGL(gemm_tiled_kernel<BNN_EPI_REPACK>, grid, block, 0, s, xp, wp, alpha, y,
+      hipLaunchKernelGGL(gemm_tiled_kernel<BNN_EPI_REPACK>, grid, block, 0, s, xp, wp, ep, y,
                          (int)M, (int)N, (int)K, kw, tiles_n, tiles);
       break;
   }

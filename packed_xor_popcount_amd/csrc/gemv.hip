@@ -48,11 +48,11 @@ constexpr int kBlocksPerCU = BNN_GEMV_BLOCKS_PER_CU;  // persistent grid size (x
 template <int EPI, int L, int VEC, int P, int XT>
 __global__ void __launch_bounds__(256)
     gemv_kernel(const void *__restrict__ xv, int64_t ldx, const uint64_t *__restrict__ wp,
-                const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
-                int kw, int kcw, int xvec) {
+                const EpiParams ep, void *__restrict__ yv, int M, int N, int K, int kw, int kcw,
+                int xvec) {
   constexpr int G = 64 / L;      // columns per wave per pass
   constexpr int CB = 4 * G * P;  // columns per block step
-  static_assert(EPI != BNN_EPI_REPACK || CB == 64, "a repack step covers 64 columns");
+  static_assert(!is_repack(EPI) || CB == 64, "a repack step covers 64 columns");
   static_assert(256 % CB == 0, "a thread's epilogue column is fixed");
   __shared__ uint32_t res[kMR][CB];
   extern __shared__ __attribute__((aligned(16))) uint64_t xs[];  // XT != 0: [rows][kcw]
@@ -128,6 +128,14 @@ __global__ void __launch_bounds__(256)
     // chunk skip the popcounts and columns past N are never stored.
     uint64_t wa[P][VEC], wb[P][VEC];
     float a_pre = 0.0f;
+    // Threshold of column nb + lane and flip word of this step's 64 columns
+    // (threshold repack; loaded here so that K = 0 has them too).
+    int32_t t_pre = 0;
+    uint64_t f_pre = 0;
+    if (EPI == kEpiRepackThr) {
+      t_pre = thr_of(ep, nb + lane, N);
+      f_pre = flip_of(ep, nb >> 6, N);
+    }
 
     for (int mb = 0; mb < M; mb += kMR) {
       const int mrows = (M - mb) < kMR ? (M - mb) : kMR;
@@ -163,7 +171,7 @@ __global__ void __launch_bounds__(256)
           // The epilogue column of this thread is fixed (CB divides 256).
           int64_t n = nb + (tid % CB);
           n = n < N ? n : N - 1;
-          a_pre = alpha[n];
+          a_pre = ep.alpha[n];
         }
 
         if constexpr (XT != 0) {
@@ -234,12 +242,12 @@ __global__ void __launch_bounds__(256)
       }
       __syncthreads();
 
-      if (EPI == BNN_EPI_REPACK) {
+      if (is_repack(EPI)) {
         if (wave == 0) {
           const int64_t n = nb + lane;
           for (int r = 0; r < mrows; ++r) {
             const int dot = (int)((uint32_t)K - 2u * res[r][lane]);
-            const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= 0);
+            const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= t_pre) ^ f_pre;
             if (lane == 0) static_cast<uint64_t *>(yv)[(int64_t)(mb + r) * nw + (nb >> 6)] = word;
           }
         }
@@ -272,12 +280,11 @@ __global__ void __launch_bounds__(256)
 template <int EPI, int L, int VEC, int P, int DT>
 __global__ void __launch_bounds__(256)
     gemv_act_kernel(const void *__restrict__ xv, int64_t ldx, const uint64_t *__restrict__ wp,
-                    const float *__restrict__ alpha, void *__restrict__ yv, int M, int N, int K,
-                    int kw) {
+                    const EpiParams ep, void *__restrict__ yv, int M, int N, int K, int kw) {
   constexpr int G = 64 / L;
   constexpr int CB = 4 * G * P;
   constexpr int kS = 4;  // activation words per lane group per round
-  static_assert(EPI != BNN_EPI_REPACK || CB == 64, "a repack step covers 64 columns");
+  static_assert(!is_repack(EPI) || CB == 64, "a repack step covers 64 columns");
   __shared__ uint32_t res[kMR][CB];
   extern __shared__ __attribute__((aligned(16))) uint64_t xs[];  // [M][kw]
 
@@ -338,8 +345,16 @@ __global__ void __launch_bounds__(256)
       if (EPI == BNN_EPI_SCALED) {
         int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
         n = n < N ? n : N - 1;
-        a_pre[p] = alpha[n];
+        a_pre[p] = ep.alpha[n];
       }
+    }
+    // Threshold of column nb + lane and flip word of the step (repack is
+    // stored by wave 0, one column per lane).
+    int32_t t_pre = 0;
+    uint64_t f_pre = 0;
+    if (EPI == kEpiRepackThr) {
+      t_pre = thr_of(ep, nb + lane, N);
+      f_pre = flip_of(ep, nb >> 6, N);
     }
     uint64_t w[P][VEC];
 #pragma unroll
@@ -396,7 +411,7 @@ __global__ void __launch_bounds__(256)
         acc[p][r] = group_sum<L>(acc[p][r]);
       }
 
-    if (EPI == BNN_EPI_REPACK) {
+    if (is_repack(EPI)) {
       __syncthreads();  // res is free (the previous step's epilogue has read it)
       if (part == 0) {
 #pragma unroll
@@ -412,7 +427,7 @@ __global__ void __launch_bounds__(256)
         const int64_t n = nb + lane;
         for (int r = 0; r < M; ++r) {
           const int dot = (int)((uint32_t)K - 2u * res[r][lane]);
-          const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= 0);
+          const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= t_pre) ^ f_pre;
           if (lane == 0) static_cast<uint64_t *>(yv)[(int64_t)r * nw + (nb >> 6)] = word;
         }
       }
@@ -441,7 +456,7 @@ struct Args {
   const void *x;
   int64_t ldx;
   const uint64_t *wp;
-  const float *alpha;
+  EpiParams ep;
   void *y;
   int M, N, K, kw, kcw, xvec;
 };
@@ -460,20 +475,20 @@ hipError_t launch_lp(const Args &a, hipStream_t s) {
     if (a.M <= kMR && a.kw > 0 && a.kw / VEC <= L && a.K % 64 == 0 && a.xvec) {
       const size_t shmem = (size_t)a.M * a.kw * sizeof(uint64_t);
       hipLaunchKernelGGL((gemv_act_kernel<EPI, L, VEC, P, XT - 1>), dim3((unsigned)blocks),
-                         dim3(256), shmem, s, a.x, a.ldx, a.wp, a.alpha, a.y, a.M, a.N, a.K,
+                         dim3(256), shmem, s, a.x, a.ldx, a.wp, a.ep, a.y, a.M, a.N, a.K,
                          a.kw);
       return hipGetLastError();
     }
   }
   const size_t shmem = XT == 0 ? 0 : (size_t)rows * a.kcw * sizeof(uint64_t);
   hipLaunchKernelGGL((gemv_kernel<EPI, L, VEC, P, XT>), dim3((unsigned)blocks), dim3(256), shmem,
-                     s, a.x, a.ldx, a.wp, a.alpha, a.y, a.M, a.N, a.K, a.kw, a.kcw, a.xvec);
+                     s, a.x, a.ldx, a.wp, a.ep, a.y, a.M, a.N, a.K, a.kw, a.kcw, a.xvec);
   return hipGetLastError();
 }
 
 template <int EPI, int L, int VEC, int XT>
 hipError_t launch_l(const Args &a, hipStream_t s) {
-  if constexpr (EPI == BNN_EPI_REPACK) {
+  if constexpr (is_repack(EPI)) {
     return launch_lp<EPI, L, VEC, XT, L / 4>(a, s);  // a step covers 64 columns
   } else {
     // One pass per step while one wave of blocks covers N (latency-bound
@@ -509,21 +524,22 @@ hipError_t launch_xt(const Args &a, int epilogue, hipStream_t s) {
   switch (epilogue) {
     case BNN_EPI_I32: return launch_epi<BNN_EPI_I32, XT>(a, s);
     case BNN_EPI_SCALED: return launch_epi<BNN_EPI_SCALED, XT>(a, s);
+    case kEpiRepackThr: return launch_epi<kEpiRepackThr, XT>(a, s);
     default: return launch_epi<BNN_EPI_REPACK, XT>(a, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const float *alpha, void *y,
+hipError_t launch_gemv(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y,
                        int64_t M, int64_t N, int64_t K, int epilogue, hipStream_t s) {
   const int kw = (int)((K + 63) / 64);
-  const Args a{xp, kw, wp, alpha, y, (int)M, (int)N, (int)K, kw, kw > 0 ? kw : 1, 0};
+  const Args a{xp, kw, wp, ep, y, (int)M, (int)N, (int)K, kw, kw > 0 ? kw : 1, 0};
   return launch_xt<0>(a, epilogue, s);
 }
 
 hipError_t launch_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *wp,
-                           const float *alpha, void *y, int64_t M, int64_t N, int64_t K,
+                           const EpiParams &ep, void *y, int64_t M, int64_t N, int64_t K,
                            int epilogue, hipStream_t s) {
   const int kw = (int)((K + 63) / 64);
   const int64_t esize = dtype == 0 ? 4 : 2;
@@ -532,7 +548,7 @@ hipError_t launch_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t
   // K-chunk per row in LDS: even (for 16-byte W loads), at most kChunkWords.
   int kcw = kw < kChunkWords ? kw : kChunkWords;
   if (kcw < 1) kcw = 1;
-  const Args a{x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, kw, kcw, xvec};
+  const Args a{x, ldx, wp, ep, y, (int)M, (int)N, (int)K, kw, kcw, xvec};
   return dtype == 0 ? launch_xt<1>(a, epilogue, s) : launch_xt<2>(a, epilogue, s);
 }
 

@@ -133,3 +133,21 @@ def test_gemv_act_validation(lib):
     assert f(FAKE, 1, 4, FAKE_ODD, FAKE, FAKE, 1, 1, 4, 0, None) == E_ALIGN
     assert f(FAKE, 1, 4, FAKE, FAKE, P(0x1004), 1, 1, 4, 2, None) == E_ALIGN
     assert f(None, 0, 4, FAKE, None, None, 0, 3, 4, 0, None) == OK
+
+
+def test_repack_thr_validation(lib):
+    f = lib.bnn_gemm_sign_repack_thr
+    # (xp, wp, thr, flip, yp, M, N, K, algo, stream)
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 1, 1, 64, 9, None) == E_ARG
+    assert f(FAKE, FAKE, FAKE, None, FAKE, -1, 1, 64, 0, None) == E_SHAPE
+    assert f(FAKE, FAKE, FAKE, None, FAKE, 1, 1, 2 ** 24 + 1, 3, None) == E_SHAPE  # MFMA limit
+    assert f(FAKE, FAKE, None, None, FAKE, 1, 1, 64, 0, None) == E_NULL            # thr
+    assert f(None, FAKE, FAKE, None, FAKE, 1, 1, 64, 0, None) == E_NULL
+    assert f(FAKE, FAKE, FAKE, None, None, 1, 1, 64, 0, None) == E_NULL
+    assert f(FAKE, FAKE, P(0x1002), None, FAKE, 1, 1, 64, 0, None) == E_ALIGN      # thr
+    assert f(FAKE, FAKE, FAKE, P(0x1004), FAKE, 1, 1, 64, 0, None) == E_ALIGN      # flip
+    assert f(FAKE, FAKE, FAKE, None, P(0x1004), 1, 1, 64, 0, None) == E_ALIGN      # yp
+    assert f(None, FAKE, None, None, None, 0, 3, 64, 0, None) == OK                # empty
+    # the threshold epilogue is reachable only through its own entry point
+    assert lib.bnn_gemm_ex(FAKE, FAKE, None, FAKE, 1, 1, 64, 3, 0, None) == E_ARG
+    assert lib.bnn_gemv_act(FAKE, 0, 64, FAKE, None, FAKE, 1, 1, 64, 3, None) == E_ARG

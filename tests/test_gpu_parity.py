@@ -218,6 +218,70 @@ def test_runs_on_a_side_stream():
 
 
 # ---------------------------------------------------------------------------
+# bnn_gemm_sign_repack_thr: per-channel threshold and flip mask
+
+
+def flags_of(mask: np.ndarray, n: int) -> np.ndarray:
+    """Per-channel flags (uint8) from a packed mask: bit c%64 of word c/64."""
+    bits = np.unpackbits(np.ascontiguousarray(mask, np.uint64).view(np.uint8), bitorder="little")
+    return bits[:n].astype(np.uint8)
+
+
+def rand_thr(rng, n, k):
+    thr = rng.integers(-k - 3, k + 3, n).astype(np.int64)
+    if n >= 6:
+        thr[:6] = [-(2 ** 31), 2 ** 31 - 1, -k - 1, -k, k, k - 1]
+    return thr.astype(np.int32)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("algo", ALGOS)
+def test_repack_thr_parity(M, N, K, algo):
+    say("repack_thr", M, N, K, "algo", algo)
+    rng = np.random.default_rng(M * 7 + N * 1013 + K * 31 + 1)
+    xg, xc = rand_packed(rng, M, K)
+    wg, wc = rand_packed(rng, N, K)
+    xd, wd = to_dev_words(xg), to_dev_words(wg)
+    thr = rand_thr(rng, N, K)
+    td = torch.from_numpy(thr).to(DEV)
+    # flip mask with garbage past column N (it must be ignored)
+    mask = rng.integers(0, 2 ** 64, size=oracle.words(N), dtype=np.uint64)
+    got = words_np(bnn.gemm_sign_repack_thr(xd, wd, td, K, to_dev_words(mask[None])[0], algo))
+    assert np.array_equal(got, oracle.sign_repack_thr(xc, wc, thr, K, flags_of(mask, N)))
+    got = words_np(bnn.gemm_sign_repack_thr(xd, wd, td, K, None, algo))
+    assert np.array_equal(got, oracle.sign_repack_thr(xc, wc, thr, K))
+    zero = torch.zeros(N, dtype=torch.int32, device=DEV)
+    got = words_np(bnn.gemm_sign_repack_thr(xd, wd, zero, K, None, algo))
+    assert np.array_equal(got, oracle.sign_repack(xc, wc, K))
+
+
+def test_repack_thr_extreme_k_on_matrix_cores():
+    # K = 2^24, the matrix-core limit: dots of exactly +-K against thresholds
+    # -K - 1, -K, K - 1, K (the fp32 bound is exact only after clamping)
+    K = 2 ** 24
+    rng = np.random.default_rng(14)
+    _, x = rand_packed(rng, 2, K)
+    w = np.stack([x[0], ~x[0], x[1], ~x[1]])
+    thr = np.array([-K - 1, -K, K - 1, K], np.int32)
+    ref = oracle.sign_repack_thr(x, w, thr, K)
+    for algo in (bnn.ALGO_MFMA, bnn.ALGO_TILED, bnn.ALGO_GEMV):
+        got = words_np(bnn.gemm_sign_repack_thr(to_dev_words(x), to_dev_words(w),
+                                                torch.from_numpy(thr).to(DEV), K, None, algo))
+        assert np.array_equal(got, ref), algo
+
+
+def test_flip_words_matches_flags():
+    rng = np.random.default_rng(15)
+    for n in (1, 63, 64, 65, 1000):
+        flags = rng.integers(0, 2, n).astype(np.uint8)
+        got = words_np(bnn.flip_words(torch.from_numpy(flags).to(DEV))[None])[0]
+        assert np.array_equal(flags_of(got, n), flags)
+        assert got.shape == (oracle.words(n),)
+        if n % 64:
+            assert int(got[-1]) >> (n % 64) == 0
+
+
+# ---------------------------------------------------------------------------
 # the five workloads at full size
 
 
@@ -307,6 +371,43 @@ def test_workload_chain_65536():
     assert_scaled_equal(y.cpu().numpy()[rows], final)
     # property at every row: hidden words have zero pad bits and the right shape
     assert h1.shape == (x.shape[0], 4) and h2.shape == (x.shape[0], 2)
+
+
+def test_workload_chain_65536_bn_folded():
+    # the same chain with a BatchNorm after each hidden binary layer, folded
+    # into per-channel thresholds and flips on the host
+    from packed_xor_popcount_amd.fold import bn_fold
+    d = workloads.make("chain_65536")
+    dims = d["dims"]
+    x = d["x"]
+    rng = np.random.default_rng(56)
+    params = []
+    for i in range(2):
+        n = d["weights"][i].shape[0]
+        k = dims[i]
+        gamma = rng.standard_normal(n)
+        beta = rng.standard_normal(n)
+        mean = rng.standard_normal(n) * np.sqrt(k)
+        std = np.abs(rng.standard_normal(n)) + 0.5
+        params.append(bn_fold(gamma, beta, mean, std, np.ones(n), k))
+    h = bnn.pack_signs(x.to(DEV))
+    wps = [bnn.pack_signs(w.to(DEV)) for w in d["weights"]]
+    hs = []
+    for i in range(2):
+        thr, flip = params[i]
+        fd = bnn.flip_words(torch.from_numpy(flip).to(DEV))
+        h = bnn.gemm_sign_repack_thr(h, wps[i], torch.from_numpy(thr).to(DEV), dims[i], fd)
+        hs.append(h)
+    y = bnn.gemm_u64_scaled(h, wps[2], d["alpha"].to(DEV), dims[2])
+    rows = np.sort(rng.choice(x.shape[0], 2048, replace=False))
+    rows[0], rows[-1] = 0, x.shape[0] - 1
+    r = oracle.pack(x.numpy()[rows])
+    for i in range(2):
+        r = oracle.sign_repack_thr(r, oracle.pack(d["weights"][i].numpy()), params[i][0], dims[i],
+                                   params[i][1])
+        assert np.array_equal(words_np(hs[i])[rows], r), i
+    ref = oracle.gemm_scaled(r, oracle.pack(d["weights"][2].numpy()), d["alpha"].numpy(), dims[2])
+    assert_scaled_equal(y.cpu().numpy()[rows], ref)
 
 
 # ---------------------------------------------------------------------------
