@@ -20,7 +20,8 @@ bf16 inputs are numpy ``uint16`` arrays of raw bit patterns.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 (identity, brute force, special cases, padding, projection table, library
-witness, scaled closed form, repack composition, worked examples).
+witness, scaled closed form, repack composition, worked examples, threshold
+repack, real-activation product).
 """
 from __future__ import annotations
 
@@ -71,9 +72,10 @@ def _load():
     lib.oracle_sign_repack.argtypes = [P, P, I64, I64, I64, P, ctypes.c_int]
     lib.oracle_dot_pairs.argtypes = [P, P, I64, P, P, I64, P]
     lib.oracle_sign_repack_thr.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_int]
+    lib.oracle_dot_signw_bf16.argtypes = [P, I64, P, I64, I64, I64, P, ctypes.c_int]
     for name in ("oracle_pack_f32", "oracle_pack_bf16", "oracle_unpack", "oracle_gemm_i32",
                  "oracle_gemm_scaled", "oracle_sign_repack", "oracle_dot_pairs",
-                 "oracle_sign_repack_thr"):
+                 "oracle_sign_repack_thr", "oracle_dot_signw_bf16"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -194,6 +196,29 @@ def sign_repack_thr(xp: np.ndarray, wp: np.ndarray, thr: np.ndarray, k: int, fli
         _load().oracle_sign_repack_thr(_ptr(xp), _ptr(wp), _ptr(thr),
                                        None if fl is None else _ptr(fl), M, N, k, _ptr(y), nthreads)
     return y
+
+
+def dot_signw_bf16(x_bits: np.ndarray, wp: np.ndarray, k: int | None = None,
+                   nthreads: int = 0) -> np.ndarray:
+    """float64 ``(M, N)``: ``sum_k x[m, k] * w_n[k]`` for real-valued bf16
+    activations (``uint16`` bit patterns, ``(M, >= k)``) and packed sign
+    weights ``wp`` ``(N, words(k))``, summed in k order in double."""
+    x_bits = np.asarray(x_bits)
+    if x_bits.dtype != np.uint16 or x_bits.ndim != 2:
+        raise TypeError("x_bits must be a 2-D uint16 array of bf16 bit patterns")
+    M, ld = x_bits.shape
+    k = ld if k is None else int(k)
+    if k > ld:
+        raise ValueError("k larger than the row length")
+    wp = np.ascontiguousarray(wp, dtype=np.uint64)
+    if wp.ndim != 2 or wp.shape[1] != words(k):
+        raise ValueError(f"packed weights must be (rows, {words(k)}) for K={k}")
+    x_bits = np.ascontiguousarray(x_bits)
+    N = wp.shape[0]
+    s = np.zeros((M, N), dtype=np.float64)
+    if M and N:
+        _load().oracle_dot_signw_bf16(_ptr(x_bits), ld, _ptr(wp), M, N, k, _ptr(s), nthreads)
+    return s
 
 
 def dot_pairs(xp: np.ndarray, wp: np.ndarray, k: int, mi, ni) -> np.ndarray:

@@ -261,3 +261,65 @@ void oracle_dot_pairs(const uint64_t *xp, const uint64_t *wp, int64_t K, const i
   free(a);
   free(b);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Real-valued activations times packed sign weights: the inference form of a
+ * layer whose weights alone are binarised (binary_nn README, "Binary
+ * Regression" and "Triton Kernel Benchmark": the eval-only packed-sign path
+ * of BinaryLinear, whose outputs differ from the dense product by rounding
+ * only).
+ *
+ *   s[m][n] = sum over k < K of x[m][k] * w_n[k],   w_n[k] in {+1, -1}
+ *
+ * with w_n[k] read from the packed row ([BME 1] encoding; pad bits never
+ * read), x given as bf16 bit patterns (row stride ldx elements) widened
+ * exactly, and the sum taken in k order in double.  For the inputs the tests
+ * use the double sum is exact; in general its error is below K * 2^-53 *
+ * sum |x|, far below fp32 rounding.  Rows are split over threads. */
+
+typedef struct {
+  const uint16_t *x;
+  int64_t ldx;
+  const int8_t *wu;
+  double *s;
+  int64_t m_begin, m_end, N, K;
+} signw_job_t;
+
+static void *signw_rows(void *arg) {
+  const signw_job_t *j = (const signw_job_t *)arg;
+  for (int64_t m = j->m_begin; m < j->m_end; ++m) {
+    for (int64_t n = 0; n < j->N; ++n) {
+      const int8_t *w = j->wu + n * j->K;
+      double acc = 0.0;
+      for (int64_t k = 0; k < j->K; ++k)
+        acc += (double)oracle_bf16_to_f32(j->x[m * j->ldx + k]) * (double)w[k];
+      j->s[m * j->N + n] = acc;
+    }
+  }
+  return NULL;
+}
+
+void oracle_dot_signw_bf16(const uint16_t *x, int64_t ldx, const uint64_t *wp, int64_t M,
+                           int64_t N, int64_t K, double *s, int nthreads) {
+  if (M <= 0 || N <= 0) return;
+  int64_t kk = K > 0 ? K : 0;
+  int8_t *wu = (int8_t *)malloc((size_t)(N * kk > 0 ? N * kk : 1));
+  oracle_unpack(wp, N, kk, wu);
+  int nt = resolve_threads(nthreads, M);
+  pthread_t th[256];
+  signw_job_t jobs[256];
+  for (int t = 0; t < nt; ++t) {
+    jobs[t].x = x;
+    jobs[t].ldx = ldx;
+    jobs[t].wu = wu;
+    jobs[t].s = s;
+    jobs[t].m_begin = M * t / nt;
+    jobs[t].m_end = M * (t + 1) / nt;
+    jobs[t].N = N;
+    jobs[t].K = kk;
+  }
+  for (int t = 1; t < nt; ++t) pthread_create(&th[t], NULL, signw_rows, &jobs[t]);
+  signw_rows(&jobs[0]);
+  for (int t = 1; t < nt; ++t) pthread_join(th[t], NULL);
+  free(wu);
+}

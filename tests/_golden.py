@@ -87,3 +87,23 @@ def pair_rows_for_dots(k: int, dots):
         assert (k - d) % 2 == 0 and abs(d) <= k, (k, d)
         w[n, : (k - d) // 2] = -1.0
     return x, w
+
+
+def _expand_values(spec: str) -> list:
+    out = []
+    for tok in spec.split():
+        if "*" in tok:
+            c, v = tok.split("*")
+            out += [float(v)] * int(c)
+        else:
+            out.append(float(tok))
+    return out
+
+
+def signw_examples():
+    """(x values as float64 array, sign string, expected s)."""
+    for xs, ws, exp in _rows("signw_examples.txt"):
+        x = np.array(_expand_values(xs), dtype=np.float64)
+        signs = _expand_signs(ws)
+        assert len(signs) == x.size, (xs, ws)
+        yield x, signs, float(exp)

@@ -355,7 +355,7 @@ def test_threads_do_not_change_results():
 def _mutant(**over):
     ns = types.SimpleNamespace(**{k: getattr(oracle, k) for k in (
         "words", "pack", "unpack", "gemm_i32", "gemm_scaled", "sign_repack", "dot_pairs",
-        "chain", "sign_f32", "sign_bf16", "sign_repack_thr")})
+        "chain", "sign_f32", "sign_bf16", "sign_repack_thr", "dot_signw_bf16")})
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -455,3 +455,135 @@ def test_pins_catch_threshold_mistakes():
     for m in bad:
         with pytest.raises(AssertionError):
             pin_repack_thr(m)
+
+
+# --------------------------------------------------------------------------
+# Real-valued bf16 activations times packed sign weights (binary_nn README,
+# "Binary Regression" / "Triton Kernel Benchmark"): s = sum_k x[k] w_n[k].
+
+
+def bf16_of(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float64 values that bf16 holds exactly (checked)."""
+    f = np.asarray(v, dtype=np.float32)
+    b = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    assert np.array_equal((b.astype(np.uint32) << np.uint32(16)).view(np.float32), f)
+    return b
+
+
+def bf16_value(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32) \
+        .astype(np.float64)
+
+
+def rand_bf16(rng, rows, k):
+    """N(0,1) values rounded to bf16 by truncation (any bf16 value will do)."""
+    f = rng.standard_normal((rows, k)).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def pin_signw_examples(o):
+    for x, signs, exp in _golden.signw_examples():
+        k = x.size
+        wp = o.pack(_golden.signs_to_f32(signs)) if k else np.zeros((1, 0), np.uint64)
+        got = o.dot_signw_bf16(bf16_of(x).reshape(1, -1), wp, k)
+        assert got.shape == (1, 1) and got[0, 0] == exp, (x, signs, got)
+
+
+def pin_signw_library_witness(o, seed=31):
+    # numpy float64 matmul of the bf16 values with independently unpacked
+    # +-1 weights; both sums are exact in double for these inputs (8-bit
+    # mantissas, exponents within 2^-20 .. 2^4, at most 2^11 terms)
+    rng = np.random.default_rng(seed)
+    for k in (1, 5, 63, 64, 65, 200, 1000, 2000):
+        M, N = 4, 9
+        xb = rand_bf16(rng, M, k)
+        xv = bf16_value(xb)
+        xv[np.abs(xv) < 2.0 ** -20] = 0.0
+        xb = bf16_of(xv)
+        wp = rand_packed(rng, N, k)
+        ref = xv @ np_unpack(wp, k).T.astype(np.float64)
+        assert np.array_equal(o.dot_signw_bf16(xb, wp, k), ref), k
+
+
+def pin_signw_one_hot(o, seed=32):
+    # x = e_k reads weight element k alone: bit order, word boundaries, pads
+    rng = np.random.default_rng(seed)
+    k = 130
+    wp = rand_packed(rng, 5, k)
+    garbage = wp | garbage_pads(rng, 5, k)
+    eye = bf16_of(np.eye(k))
+    ref = np_unpack(wp, k).T.astype(np.float64)     # [k][n]
+    assert np.array_equal(o.dot_signw_bf16(eye, wp, k), ref)
+    assert np.array_equal(o.dot_signw_bf16(eye, garbage, k), ref)
+
+
+def pin_signw_binary_reduction(o, seed=33):
+    # +-1 activations reduce it to the integer binary product of the packed
+    # signs, i.e. K - 2 popcount(x xor w) computed here with numpy bit ops
+    rng = np.random.default_rng(seed)
+    for k in (1, 64, 100, 777):
+        xp, wp = rand_packed(rng, 3, k), rand_packed(rng, 6, k)
+        xv = np_unpack(xp, k).astype(np.float64)
+        mask = np_tail_mask(k)
+        d = np.bitwise_count((xp[:, None, :] ^ wp[None, :, :]) & mask).sum(axis=2).astype(np.int64)
+        assert np.array_equal(o.dot_signw_bf16(bf16_of(xv), wp, k), (k - 2 * d).astype(np.float64))
+
+
+def pin_signw_strided(o, seed=34):
+    # rows read with their stride; columns past k are never read
+    rng = np.random.default_rng(seed)
+    big = rand_bf16(rng, 3, 90)
+    wp = rand_packed(rng, 4, 70)
+    ref = o.dot_signw_bf16(np.ascontiguousarray(big[:, :70]), wp, 70)
+    assert np.array_equal(o.dot_signw_bf16(big, wp, 70), ref)
+    poisoned = big.copy()
+    poisoned[:, 70:] = 0x7FC0  # NaN past k
+    assert np.array_equal(o.dot_signw_bf16(poisoned, wp, 70), ref)
+
+
+_SIGNW_PINS = [pin_signw_examples, pin_signw_library_witness, pin_signw_one_hot,
+               pin_signw_binary_reduction, pin_signw_strided]
+
+
+@pytest.mark.parametrize("pin", _SIGNW_PINS, ids=[p.__name__ for p in _SIGNW_PINS])
+def test_signw_pins(pin):
+    pin(oracle)
+
+
+def _msb_first_words(p):
+    return _msb_first(np.ascontiguousarray(p, np.uint64))
+
+
+def _signw_zero_columns(x, k, keep):
+    """Copy of x (bf16 bits) with columns keep .. k-1 set to +0."""
+    x = np.array(x, dtype=np.uint16, copy=True)
+    x[:, keep:k] = 0
+    return x
+
+
+def test_signw_pins_catch_planted_mistakes():
+    o = oracle
+
+    def kk(x, k):
+        return np.asarray(x).shape[1] if k is None else k
+
+    mutants = {
+        "weights negated": lambda x, wp, k=None, nthreads=0: -o.dot_signw_bf16(x, wp, k),
+        "bit order msb-first": lambda x, wp, k=None, nthreads=0: o.dot_signw_bf16(
+            x, _msb_first_words(wp), k),
+        "last element dropped": lambda x, wp, k=None, nthreads=0: o.dot_signw_bf16(
+            _signw_zero_columns(x, kk(x, k), max(kk(x, k) - 1, 0)), wp, k),
+        "tail word dropped": lambda x, wp, k=None, nthreads=0: o.dot_signw_bf16(
+            _signw_zero_columns(x, kk(x, k), 64 * (kk(x, k) // 64)), wp, k),
+        "first row for all": lambda x, wp, k=None, nthreads=0: o.dot_signw_bf16(
+            np.repeat(np.asarray(x)[:1], np.asarray(x).shape[0], axis=0), wp, k),
+    }
+    for name, f in mutants.items():
+        m = _mutant(dot_signw_bf16=f)
+        caught = 0
+        for pin in _SIGNW_PINS:
+            try:
+                pin(m)
+            except (AssertionError, ValueError):
+                caught += 1
+        assert caught, name
