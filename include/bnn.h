@@ -199,6 +199,40 @@ bnn_status bnn_gemm_sign_repack_thr(const uint64_t *xp, const uint64_t *wp, cons
                                     int64_t K, int algo, void *stream);
 
 /*
+ * bnn_gemm_signw_bf16 -- real-valued bf16 activations times packed sign
+ * weights: y[m][n] = alpha[n] * sum_{k<K} x[m][k] * w_n[k], with w_n[k] = +1
+ * for bit 0 and -1 for bit 1 of packed row n (the bnn_pack_signs layout).
+ * This is the inference form of a layer whose weights alone are binarised
+ * (binary_nn README, "Binary Regression" and "Triton Kernel Benchmark": the
+ * eval-only packed-sign path of BinaryLinear); the weights keep their 1-bit
+ * form ("Binary Math Effectiveness", section 2.2), the activations stay real.
+ *
+ * Arithmetic: every product x*(+-1) is exact; the K-term sum is accumulated
+ * in fp32 in an order the kernel chooses (a tree of v_dot2 / MFMA partial
+ * sums), then multiplied by alpha[n] once.  The result therefore differs
+ * from the exact value by fp32 summation rounding only: at most
+ * |alpha| * gamma * sum_k |x[m][k]| + 2^-23 |y|, gamma = K 2^-23 / (1 - K 2^-23),
+ * and it is exact whenever every partial sum is representable in fp32 (for
+ * example integer-valued activations with |sum| < 2^24).  Inputs must be
+ * finite.  Elements past K and pad bits are never used.
+ *
+ *   x      M rows of bf16 values (raw 16-bit patterns), row stride ldx >= K
+ *          elements, 2-byte aligned.
+ *   wp     N x bnn_words(K) packed sign weights, 8-byte aligned.
+ *   alpha  N fp32 per-output-channel scales, 4-byte aligned, or NULL for
+ *          none (alpha = 1; the sum is stored as is).
+ *   y      M x N fp32 output, row-major, 4-byte aligned.
+ *   algo   BNN_ALGO_AUTO, BNN_ALGO_GEMV (small M: M <= 8 and the rows fit in
+ *          64 KiB of LDS, else BNN_E_SHAPE) or BNN_ALGO_MFMA (any shape; bf16
+ *          matrix cores).  The two kernels sum in different orders, so
+ *          their results may differ by rounding.  BNN_ALGO_TILED -> BNN_E_ARG.
+ * K = 0 gives y = 0 (times alpha).  Errors: BNN_E_SHAPE (negative or too
+ * large sizes, ldx < K), BNN_E_NULL, BNN_E_ALIGN, BNN_E_ARG, BNN_E_LAUNCH.
+ */
+bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, const float *alpha,
+                               float *y, int64_t M, int64_t N, int64_t K, int algo, void *stream);
+
+/*
  * bnn_gemm_ex -- the general form of the three products above, with an
  * explicit kernel family (see bnn_algo; the matrix-core family takes the
  * same exact integer sum of +-1 products on the MFMA units, which "Binary

@@ -27,7 +27,8 @@ __all__ = [
     "BnnError", "EPI_I32", "EPI_SCALED", "EPI_REPACK", "ALGO_AUTO", "ALGO_GEMV", "ALGO_TILED",
     "ALGO_MFMA",
     "library", "library_path", "words", "pack_signs", "gemm_u64", "gemm_u64_scaled",
-    "gemm_sign_repack", "gemm_sign_repack_thr", "flip_words", "gemm_ex", "gemv_act", "version",
+    "gemm_sign_repack", "gemm_sign_repack_thr", "flip_words", "gemm_signw_bf16", "gemm_ex",
+    "gemv_act", "version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +40,7 @@ ALGO_AUTO, ALGO_GEMV, ALGO_TILED, ALGO_MFMA = 0, 1, 2, 3
 
 EXPORTED = ("bnn_words", "bnn_status_str", "bnn_version", "bnn_pack_signs", "bnn_gemm_u64",
             "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex", "bnn_gemv_act",
-            "bnn_gemm_sign_repack_thr")
+            "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16")
 
 
 class BnnError(RuntimeError):
@@ -73,8 +74,9 @@ def library():
     lib.bnn_gemm_ex.argtypes = [P, P, P, P, I64, I64, I64, I, I, P]
     lib.bnn_gemv_act.argtypes = [P, I, I64, P, P, P, I64, I64, I64, I, P]
     lib.bnn_gemm_sign_repack_thr.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
+    lib.bnn_gemm_signw_bf16.argtypes = [P, I64, P, P, P, I64, I64, I64, I, P]
     for name in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack",
-                 "bnn_gemm_ex", "bnn_gemv_act", "bnn_gemm_sign_repack_thr"):
+                 "bnn_gemm_ex", "bnn_gemv_act", "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -263,3 +265,29 @@ def flip_words(flags: torch.Tensor) -> torch.Tensor:
         raise ValueError("flags must be 1-D")
     signs = torch.where(flags != 0, -1.0, 1.0).to(torch.float32).reshape(1, -1)
     return pack_signs(signs)[0]
+
+
+def gemm_signw_bf16(x, wp, K=None, alpha=None, algo=ALGO_AUTO, out=None):
+    """fp32 ``(M, N)``: ``alpha[n] * sum_k x[m, k] * w_n[k]`` for real-valued
+    bf16 activations ``x`` (2-D CUDA tensor, unit stride along the last
+    dimension; the first ``K`` columns are used) and packed sign weights
+    ``wp`` (bnn_gemm_signw_bf16).  ``alpha`` is None (no scale) or a
+    contiguous float32 ``(N,)``; ``algo`` is ALGO_AUTO, ALGO_GEMV or ALGO_MFMA."""
+    _need_cuda("x", x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit stride along its last dimension")
+    M, cols = x.shape
+    K = cols if K is None else int(K)
+    N = _packed("wp", wp, K)
+    if alpha is not None:
+        _need_cuda("alpha", alpha)
+        if alpha.dtype != torch.float32 or alpha.shape != (N,) or not alpha.is_contiguous():
+            raise ValueError("alpha must be a contiguous float32 tensor of shape (N,)")
+    out = _out_for(EPI_SCALED, M, N, x.device, out)
+    ldx = x.stride(0) if M > 1 else max(cols, 1)
+    st = library().bnn_gemm_signw_bf16(_ptr(x), ldx, _ptr(wp), _ptr(alpha), _ptr(out), M, N, K,
+                                       int(algo), _stream(x))
+    _check(st, "bnn_gemm_signw_bf16")
+    return out

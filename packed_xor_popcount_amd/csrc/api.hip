@@ -125,6 +125,27 @@ bnn_status bnn_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t *w
                                             static_cast<hipStream_t>(stream)));
 }
 
+bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, const float *alpha,
+                               float *y, int64_t M, int64_t N, int64_t K, int algo, void *stream) {
+  if (algo != BNN_ALGO_AUTO && algo != BNN_ALGO_GEMV && algo != BNN_ALGO_MFMA) return BNN_E_ARG;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim || ldx < K ||
+      ldx >= kMaxDim)
+    return BNN_E_SHAPE;
+  const int64_t kw = bnn_words(K);
+  if ((M * K > 0 && !x) || (N * kw > 0 && !wp) || (M * N > 0 && !y)) return BNN_E_NULL;
+  if (misaligned(x, 2) || misaligned(wp, 8) || misaligned(y, 4) || misaligned(alpha, 4))
+    return BNN_E_ALIGN;
+  if (M == 0 || N == 0) return BNN_OK;
+  const bool gemv_ok = bnn::signw_gemv_fits(M, K);
+  if (algo == BNN_ALGO_GEMV && !gemv_ok) return BNN_E_SHAPE;
+  if (algo == BNN_ALGO_AUTO) algo = gemv_ok ? BNN_ALGO_GEMV : BNN_ALGO_MFMA;
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (algo == BNN_ALGO_GEMV)
+    return launch_status(bnn::launch_signw_gemv(xb, ldx, wp, alpha, y, M, N, K, s));
+  return launch_status(bnn::launch_signw_mfma(xb, ldx, wp, alpha, y, M, N, K, s));
+}
+
 bnn_status bnn_gemm_u64(const uint64_t *xp, const uint64_t *wp, int32_t *y, int64_t M, int64_t N,
                         int64_t K, void *stream) {
   return bnn_gemm_ex(xp, wp, nullptr, y, M, N, K, BNN_EPI_I32, BNN_ALGO_AUTO, stream);

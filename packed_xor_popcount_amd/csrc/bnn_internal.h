@@ -50,6 +50,20 @@ hipError_t launch_gemv_act(const void *x, int dtype, int64_t ldx, const uint64_t
                            const EpiParams &ep, void *y, int64_t M, int64_t N, int64_t K,
                            int epilogue, hipStream_t s);
 
+// Real-valued bf16 activations times packed sign weights (bnn_gemm_signw_bf16):
+// y[m][n] = alpha[n] * sum_k x[m][k] * w_n[k]; alpha may be null (no scale).
+// The GEMV form (small M) holds the activation rows in LDS, at most this many
+// bytes; signw_gemv_fits tells whether a shape qualifies.
+constexpr size_t kSignwGemvMaxLds = 64 * 1024;
+size_t signw_gemv_lds_bytes(int64_t M, int64_t kw, int vec);
+bool signw_gemv_fits(int64_t M, int64_t K);
+hipError_t launch_signw_gemv(const uint16_t *x, int64_t ldx, const uint64_t *wp,
+                             const float *alpha, float *y, int64_t M, int64_t N, int64_t K,
+                             hipStream_t s);
+hipError_t launch_signw_mfma(const uint16_t *x, int64_t ldx, const uint64_t *wp,
+                             const float *alpha, float *y, int64_t M, int64_t N, int64_t K,
+                             hipStream_t s);
+
 // Threshold-repack operands, loaded by the kernels before their K loops from
 // clamped (always in-bounds) indexes: the threshold of output column n, and
 // the flip word of 64-column group wi with its bits past column N cleared

@@ -1,0 +1,464 @@
+// signw.hip -- real-valued bf16 activations times packed sign weights:
+//
+//   y[m][n] = alpha[n] * sum_k x[m][k] * w_n[k],   w_n[k] = +1 (bit 0) / -1 (bit 1)
+//
+// the inference form of a layer whose weights alone are binarised (binary_nn
+// README, "Binary Regression" and "Triton Kernel Benchmark": BinaryLinear's
+// eval-only packed-sign path; the weight encoding is that of "Binary Math
+// Effectiveness -- why / how / when", section 1).  The weights keep their
+// 1-bit packed form (32x fewer bytes than fp32, section 2.2 of the same
+// page); the activations stay real, so the result is a floating-point sum
+// (products exact, fp32 accumulation) rather than an integer.
+//
+// Both kernels turn two weight bits into a pair of bf16 +-1 values with two
+// VALU operations.  For a 32-bit chunk c of a packed row (elements
+// 32q .. 32q+31) the pair register for position p (0..15) is
+//
+//   ((c << (15 - p)) & 0x80008000) | 0x3F803F80
+//
+// i.e. bf16 +1.0 (0x3F80) in both halves with bit p of c as the sign of the
+// low half and bit p+16 as the sign of the high half.  The activations are
+// staged in the matching order: the 32-bit word for position p holds
+// (x[32q + p], x[32q + p + 16]).  Elements past K are staged as +0, so the
+// pad bits of the last word never contribute.
+//
+//  * gemv_signw_kernel (small M, weight-streaming, VALU): L lanes share one
+//    column with coalesced 16-byte W loads; each pair of elements is one
+//    v_dot2_f32_bf16 against the activation pair held in LDS; the L partial
+//    sums are combined with DPP moves.
+//  * gemm_signw_kernel (larger M, matrix cores): v_mfma_f32_32x32x16_bf16
+//    with the activation tile staged in LDS (pair order) and the weight
+//    fragments unpacked in registers from the packed words, which every lane
+//    loads straight from L2.  Blocks are mapped so that the tiles of one
+//    8th of the rows run on one XCD (its L2 then reads those rows once).
+#include "../../include/bnn.h"
+#include "bnn_internal.h"
+
+namespace bnn {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t kSignMask = 0x80008000u;
+constexpr uint32_t kPlusOnes = 0x3F803F80u;  // bf16 (+1.0, +1.0)
+
+// Pair register of weight bits p and p + 16 of chunk c (see the header).
+// The constants come in as VGPR operands (gfx9 VOP3 takes no literal).
+__device__ __forceinline__ uint32_t sign_pair(uint32_t c_shifted, uint32_t mask, uint32_t ones) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(c_shifted), "v"(mask), "v"(ones));
+  return r;
+}
+
+__device__ __forceinline__ float dot2(uint32_t xpair, uint32_t wpair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xpair),
+                                         __builtin_bit_cast(bf16x2, wpair), acc, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of v over aligned groups of L lanes (every lane of a group receives it).
+template <int L>
+__device__ __forceinline__ float group_sum_f32(float v) {
+  if (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm 1,0,3,2
+  if (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm 2,3,0,1
+  if (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if (L >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if (L >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  if (L >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// bf16 element k of row m (k may be past K: then +0).
+__device__ __forceinline__ uint32_t x_at(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
+                                         int64_t K) {
+  return k < K ? (uint32_t)x[m * ldx + k] : 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel for small M.
+
+constexpr int kGemvRows = 8;          // activation rows per launch of the GEMV form
+constexpr int kUnitPadBytes = 16;     // LDS pad per unit (spreads lanes over banks)
+
+template <int L, int VEC, int P, bool SCALED>
+__global__ void __launch_bounds__(256)
+    gemv_signw_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint64_t *__restrict__ wp,
+                      const float *__restrict__ alpha, float *__restrict__ y, int M, int N, int K,
+                      int kw) {
+  constexpr int G = 64 / L;
+  constexpr int CB = 4 * G * P;
+  constexpr int kUnitBytes = VEC * 128 + kUnitPadBytes;  // 2 chunks of 64 B per word
+  extern __shared__ __attribute__((aligned(16))) unsigned char xs[];  // [M][units][kUnitBytes]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane / L;
+  const int part = lane % L;
+  const int units = kw / VEC;
+  const int nsteps = (N + CB - 1) / CB;
+  const uint32_t mask = kSignMask, ones = kPlusOnes;
+
+  // Stage the activation rows once per block in pair order: word p of chunk
+  // q holds (x[32q + p], x[32q + p + 16]).
+  {
+    const int chunks = units * VEC * 2;
+    const int total = M * chunks * 16;
+    for (int i = tid; i < total; i += 256) {
+      const int p = i & 15;
+      const int rq = i >> 4;
+      const int m = rq / chunks, q = rq - m * chunks;
+      const int64_t k = (int64_t)q * 32 + p;
+      const uint32_t v = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 16, K) << 16);
+      const int u = q / (VEC * 2), qi = q - u * (VEC * 2);
+      *reinterpret_cast<uint32_t *>(xs + ((size_t)m * units + u) * kUnitBytes + qi * 64 + p * 4) = v;
+    }
+    __syncthreads();
+  }
+
+  for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
+    const int64_t nb = (int64_t)step * CB;
+    float a_pre[P];
+    const uint64_t *wrow[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+      n = n < N ? n : N - 1;
+      wrow[p] = wp + n * kw;
+      a_pre[p] = SCALED ? alpha[n] : 1.0f;
+    }
+    float acc[P][kGemvRows];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r) acc[p][r] = 0.0f;
+
+    for (int u = part; u < units; u += L) {
+      uint64_t w[P][VEC];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint64_t *src = wrow[p] + (int64_t)u * VEC;
+        if (VEC == 2) {
+          const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+          w[p][0] = t.x;
+          w[p][VEC - 1] = t.y;
+        } else {
+          w[p][0] = src[0];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // chunk qi = 2v + h of this unit: 16 pair registers per column
+          uint32_t b[P][16];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const uint32_t c = (uint32_t)(w[p][v] >> (32 * h));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) b[p][j] = sign_pair(c << (15 - j), mask, ones);
+          }
+#pragma unroll
+          for (int r = 0; r < kGemvRows; ++r) {
+            if (r >= M) break;
+            const unsigned char *xr =
+                xs + ((size_t)r * units + u) * kUnitBytes + (2 * v + h) * 64;
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+              const uint4 xv = *reinterpret_cast<const uint4 *>(xr + 16 * j4);
+#pragma unroll
+              for (int p = 0; p < P; ++p) {
+                float a = acc[p][r];
+                a = dot2(xv.x, b[p][4 * j4 + 0], a);
+                a = dot2(xv.y, b[p][4 * j4 + 1], a);
+                a = dot2(xv.z, b[p][4 * j4 + 2], a);
+                a = dot2(xv.w, b[p][4 * j4 + 3], a);
+                acc[p][r] = a;
+              }
+            }
+          }
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int r = 0; r < kGemvRows; ++r) {
+        if (r >= M) break;
+        acc[p][r] = group_sum_f32<L>(acc[p][r]);
+      }
+    if (part == 0) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+          if (r >= M) break;
+          y[(int64_t)r * N + n] = SCALED ? __fmul_rn(acc[p][r], a_pre[p]) : acc[p][r];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel.
+//
+// v_mfma_f32_32x32x16_bf16: lane l supplies row / column l % 32 and, in its
+// four registers, 8 of the 16 k values (lanes 0-31 one half, 32-63 the other;
+// which k go in which register is free as long as A and B agree).  For the
+// 32-element chunk q of a 64-element block step, MFMA t (0, 1), lane half h
+// and register j hold the element pair (p, p + 16) with p = 8t + 4h + j.
+// The 32 x 32 output layout: lane l, register v -> row 8(v/4) + 4(l/32) +
+// v%4, column l%32.
+
+constexpr int kBK = 64;                       // elements of K per block step (one W word)
+constexpr int kARowBytes = 2 * 64 + 16;       // two chunks of 64 B + pad
+
+template <int WR, int WC, int RB, int CB, bool SCALED, bool XV8>
+__global__ void __launch_bounds__(256)
+    gemm_signw_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint64_t *__restrict__ wp,
+                      const float *__restrict__ alpha, float *__restrict__ y, int M, int N, int K,
+                      int kw, int tiles_m, int tiles_n) {
+  static_assert(WR * WC == 4, "4 waves per block");
+  constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
+  constexpr int kPieces = BM * 8;            // 16-byte A fragments per block step
+  static_assert(kPieces % 256 == 0, "whole fragments per thread");
+  constexpr int kPerThread = kPieces / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char as[BM * kARowBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int li = lane & 31;
+
+  // XCD-aware tile order: hardware places block b on XCD b % 8, so block b
+  // takes logical tile (b % 8) * per + b / 8 and each XCD owns a contiguous
+  // range of tiles (rows of X are then fetched by one L2).
+  const int nblocks = tiles_m * tiles_n;
+  const int per = (nblocks + 7) >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  // Grids that are not a multiple of 8 fall back to the plain order.
+  const int tile = (nblocks % 8 == 0) ? xcd * per + slot : (int)blockIdx.x;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int m0 = tm * BM + (wave / WC) * (RB * 32);
+  const int n0 = tn * BN + (wave % WC) * (CB * 32);
+
+  // Weight words of this lane's columns (clamped; columns past N are never stored).
+  const uint64_t *bcol[CB];
+  float a_pre[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    int n = n0 + cb * 32 + li;
+    n = n < N ? n : N - 1;
+    bcol[cb] = wp + (int64_t)n * kw;
+    a_pre[cb] = SCALED ? alpha[n] : 1.0f;
+  }
+
+  // A fragment pieces staged by this thread: fragment f = tid + 256 i is
+  // (row f / 8, chunk (f / 4) & 1, t = (f / 2) & 1, h = f & 1); it holds the
+  // four pairs (x[b + j], x[b + j + 16]), b = 32 chunk + 8t + 4h.
+  const int64_t row_lim = M - 1;
+  auto load_a = [&](int kb, uint32_t (&lo)[kPerThread][2], uint32_t (&hi)[kPerThread][2]) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int f = tid + 256 * i;
+      int64_t m = (int64_t)tm * BM + (f >> 3);
+      m = m < row_lim ? m : row_lim;
+      const int64_t k = (int64_t)kb * kBK + 32 * ((f >> 2) & 1) + 8 * ((f >> 1) & 1) + 4 * (f & 1);
+      if (XV8 && k + 20 <= K) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(x + m * ldx + k);
+        const uint2 b = *reinterpret_cast<const uint2 *>(x + m * ldx + k + 16);
+        lo[i][0] = a.x; lo[i][1] = a.y;
+        hi[i][0] = b.x; hi[i][1] = b.y;
+      } else {
+        lo[i][0] = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 1, K) << 16);
+        lo[i][1] = x_at(x, ldx, m, k + 2, K) | (x_at(x, ldx, m, k + 3, K) << 16);
+        hi[i][0] = x_at(x, ldx, m, k + 16, K) | (x_at(x, ldx, m, k + 17, K) << 16);
+        hi[i][1] = x_at(x, ldx, m, k + 18, K) | (x_at(x, ldx, m, k + 19, K) << 16);
+      }
+    }
+  };
+  auto store_a = [&](const uint32_t (&lo)[kPerThread][2], const uint32_t (&hi)[kPerThread][2]) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int f = tid + 256 * i;
+      uint4 v;  // pairs j = 0..3: low half from lo, high half from hi
+      v.x = __builtin_amdgcn_perm(hi[i][0], lo[i][0], 0x05040100u);
+      v.y = __builtin_amdgcn_perm(hi[i][0], lo[i][0], 0x07060302u);
+      v.z = __builtin_amdgcn_perm(hi[i][1], lo[i][1], 0x05040100u);
+      v.w = __builtin_amdgcn_perm(hi[i][1], lo[i][1], 0x07060302u);
+      *reinterpret_cast<uint4 *>(as + (f >> 3) * kARowBytes + (f & 7) * 16) = v;
+    }
+  };
+
+  v16f acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
+
+  const int nsteps = (K + kBK - 1) / kBK;  // == kw
+  const uint32_t mask = kSignMask, ones = kPlusOnes;
+  const int wrow = (wave / WC) * (RB * 32);  // this wave's first row inside the block tile
+
+  uint32_t lo[kPerThread][2], hi[kPerThread][2];
+  uint64_t wcur[CB];
+  if (nsteps > 0) {
+    load_a(0, lo, hi);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wcur[cb] = bcol[cb][0];
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    store_a(lo, hi);
+    __syncthreads();
+    // prefetch the next step (clamped to the last one: in bounds, unused)
+    const int sn = s + 1 < nsteps ? s + 1 : s;
+    uint64_t wnext[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wnext[cb] = bcol[cb][sn];
+    load_a(sn, lo, hi);
+
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      // weight chunk q of each column, pre-shifted by 4 for lane half 0
+      uint32_t cq[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t c = (uint32_t)(wcur[cb] >> (32 * q));
+        cq[cb] = h ? c : (c << 4);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 bfr[CB];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          uint32_t r4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) r4[j] = sign_pair(cq[cb] << (11 - 8 * t - j), mask, ones);
+          bfr[cb] = __builtin_bit_cast(bf16x8, make_uint4(r4[0], r4[1], r4[2], r4[3]));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint4 av = *reinterpret_cast<const uint4 *>(
+              as + (wrow + rb * 32 + li) * kARowBytes + q * 64 + t * 32 + h * 16);
+          const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[cb], acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wcur[cb] = wnext[cb];
+    __syncthreads();  // the tile is consumed before the next store
+  }
+
+  const int64_t ld = N;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int mt = m0 + rb * 32 + 4 * h;
+    const bool full_rows = m0 + rb * 32 + 32 <= M;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = n0 + cb * 32 + li;
+      if (n >= N) continue;
+      float *p = y + (int64_t)mt * ld + n;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int dr = 8 * (v >> 2) + (v & 3);
+        if (full_rows || mt + dr < M)
+          p[dr * ld] = SCALED ? __fmul_rn(acc[rb][cb][v], a_pre[cb]) : acc[rb][cb][v];
+      }
+    }
+  }
+}
+
+template <int L, int VEC, int P, bool SCALED>
+hipError_t launch_gemv_lp(const uint16_t *x, int64_t ldx, const uint64_t *wp, const float *alpha,
+                          float *y, int M, int N, int K, int kw, hipStream_t s) {
+  constexpr int CB = 4 * (64 / L) * P;
+  const int64_t steps = ((int64_t)N + CB - 1) / CB;
+  const int64_t cap = 256 * 8;
+  const int64_t blocks = steps < cap ? steps : cap;
+  const size_t shmem = signw_gemv_lds_bytes(M, kw, VEC);
+  hipLaunchKernelGGL((gemv_signw_kernel<L, VEC, P, SCALED>), dim3((unsigned)blocks), dim3(256),
+                     shmem, s, x, ldx, wp, alpha, y, M, N, K, kw);
+  return hipGetLastError();
+}
+
+template <int VEC, bool SCALED>
+hipError_t launch_gemv_vec(const uint16_t *x, int64_t ldx, const uint64_t *wp, const float *alpha,
+                           float *y, int M, int N, int K, int kw, hipStream_t s) {
+  const int units = kw / VEC;
+#define BNN_SIGNW_L(LL) return launch_gemv_lp<LL, VEC, 1, SCALED>(x, ldx, wp, alpha, y, M, N, K, kw, s);
+  if (units <= 4) BNN_SIGNW_L(4)
+  if (units <= 8) BNN_SIGNW_L(8)
+  if (units <= 16) BNN_SIGNW_L(16)
+  if (units <= 32) BNN_SIGNW_L(32)
+  BNN_SIGNW_L(64)
+#undef BNN_SIGNW_L
+}
+
+template <bool SCALED, bool XV8>
+hipError_t launch_mfma_cfg(const uint16_t *x, int64_t ldx, const uint64_t *wp, const float *alpha,
+                           float *y, int M, int N, int K, hipStream_t s) {
+  constexpr int WR = 2, WC = 2, RB = 2, CB = 2;
+  constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
+  const int kw = (K + 63) / 64;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_signw_kernel<WR, WC, RB, CB, SCALED, XV8>),
+                     dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, x, ldx, wp, alpha, y, M,
+                     N, K, kw, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t signw_gemv_lds_bytes(int64_t M, int64_t kw, int vec) {
+  const int64_t units = vec == 2 ? kw / 2 : kw;
+  return (size_t)(M * units * (vec * 128 + kUnitPadBytes));
+}
+
+bool signw_gemv_fits(int64_t M, int64_t K) {
+  const int64_t kw = (K + 63) / 64;
+  return M >= 1 && M <= kGemvRows && K > 0 && signw_gemv_lds_bytes(M, kw, 1) <= kSignwGemvMaxLds;
+}
+
+hipError_t launch_signw_gemv(const uint16_t *x, int64_t ldx, const uint64_t *wp,
+                             const float *alpha, float *y, int64_t M, int64_t N, int64_t K,
+                             hipStream_t s) {
+  const int kw = (int)((K + 63) / 64);
+  const bool vec2 = kw % 2 == 0 && ((uintptr_t)wp % 16 == 0);
+  if (alpha) {
+    return vec2 ? launch_gemv_vec<2, true>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, kw, s)
+                : launch_gemv_vec<1, true>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, kw, s);
+  }
+  return vec2 ? launch_gemv_vec<2, false>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, kw, s)
+              : launch_gemv_vec<1, false>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, kw, s);
+}
+
+hipError_t launch_signw_mfma(const uint16_t *x, int64_t ldx, const uint64_t *wp,
+                             const float *alpha, float *y, int64_t M, int64_t N, int64_t K,
+                             hipStream_t s) {
+  // 8-byte activation loads need 8-byte aligned row starts.
+  const bool xv8 = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0 || M == 1);
+  if (alpha) {
+    return xv8 ? launch_mfma_cfg<true, true>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s)
+               : launch_mfma_cfg<true, false>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s);
+  }
+  return xv8 ? launch_mfma_cfg<false, true>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s)
+             : launch_mfma_cfg<false, false>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s);
+}
+
+}  // namespace bnn

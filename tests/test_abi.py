@@ -151,3 +151,22 @@ def test_repack_thr_validation(lib):
     # the threshold epilogue is reachable only through its own entry point
     assert lib.bnn_gemm_ex(FAKE, FAKE, None, FAKE, 1, 1, 64, 3, 0, None) == E_ARG
     assert lib.bnn_gemv_act(FAKE, 0, 64, FAKE, None, FAKE, 1, 1, 64, 3, None) == E_ARG
+
+
+def test_signw_validation(lib):
+    f = lib.bnn_gemm_signw_bf16
+    # (x, ldx, wp, alpha, y, M, N, K, algo, stream)
+    assert f(FAKE, 64, FAKE, None, FAKE, 1, 1, 64, bnn.ALGO_TILED, None) == E_ARG
+    assert f(FAKE, 64, FAKE, None, FAKE, 1, 1, 64, 9, None) == E_ARG
+    assert f(FAKE, 63, FAKE, None, FAKE, 1, 1, 64, 0, None) == E_SHAPE      # ldx < K
+    assert f(FAKE, 64, FAKE, None, FAKE, -1, 1, 64, 0, None) == E_SHAPE
+    assert f(FAKE, 64, FAKE, None, FAKE, 9, 1, 64, bnn.ALGO_GEMV, None) == E_SHAPE  # M > 8
+    assert f(FAKE, 2 ** 20, FAKE, None, FAKE, 1, 1, 2 ** 20, bnn.ALGO_GEMV, None) == E_SHAPE
+    assert f(None, 64, FAKE, None, FAKE, 1, 1, 64, 0, None) == E_NULL
+    assert f(FAKE, 64, None, None, FAKE, 1, 1, 64, 0, None) == E_NULL
+    assert f(FAKE, 64, FAKE, None, None, 1, 1, 64, 0, None) == E_NULL
+    assert f(P(0x1001), 64, FAKE, None, FAKE, 1, 1, 64, 0, None) == E_ALIGN  # bf16 x
+    assert f(FAKE, 64, FAKE_ODD, None, FAKE, 1, 1, 64, 0, None) == E_ALIGN
+    assert f(FAKE, 64, FAKE, P(0x1002), FAKE, 1, 1, 64, 0, None) == E_ALIGN  # alpha
+    assert f(FAKE, 64, FAKE, None, P(0x1002), 1, 1, 64, 0, None) == E_ALIGN  # y
+    assert f(None, 64, FAKE, None, None, 0, 3, 64, 0, None) == OK            # empty
