@@ -47,6 +47,8 @@ ALU_PEAK_BINARY_OPS = VALU_LANE_OPS / 4 * 128
 # Dense FP4 MFMA peak of MI355X (published): 10.1 PFLOP/s.  The matrix-core
 # kernel encodes +-1 as FP4, so one binary MAC is one FP4 MAC (2 ops).
 MFMA_FP4_PEAK_OPS = 10.1e15
+# Dense bf16 MFMA peak of MI355X (published): 2.5 PFLOP/s.
+MFMA_BF16_PEAK = 2.5e15
 
 
 def log(*a):
@@ -59,7 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="gemv_4096",
-                    choices=["gemv_4096", "ffn_4096", "chain_65536"])
+                    choices=["gemv_4096", "ffn_4096", "chain_65536", "signw_gemv_4096",
+                             "signw_16384"])
     ap.add_argument("--ring", type=int, default=256, help="distinct weight copies (gemv)")
     ap.add_argument("--rows", type=int, default=None,
                     help="gemv only: override N (weight rows) for the streaming-rate variant")
@@ -128,6 +131,48 @@ GEMV_SOURCES = ["gemv.hip", "sign_bits.h", "bnn_internal.h"]
 MFMA_SOURCES = ["gemm_mfma.hip", "bnn_internal.h"]
 
 
+def ring_steps_ms(step, R, steps, warmup, eager):
+    """ms per step of `steps` calls step(i % R): eager warmup, then R steps
+    (one per ring entry) captured in a HIP graph and replayed, timed with HIP
+    events on torch's current stream (the capture's launch stream).  With
+    `eager` the steps are plain launches (for counter collection)."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for i in range(max(warmup, 1)):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    def graph_of(n):
+        gr = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(dev)
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(gr, stream=s):
+                for j in range(n):
+                    step(j % R)
+        torch.cuda.synchronize()
+        return gr
+
+    if eager:
+        return timed(lambda: [step(i % R) for i in range(steps)], 1, stream) / steps
+    full, rem = divmod(steps, R)
+    g_full = graph_of(R) if full else None
+    g_rem = graph_of(rem) if rem else None
+    for gr in (g_full, g_rem):
+        if gr is not None:
+            gr.replay()
+    torch.cuda.synchronize()
+
+    def run_steps():
+        for _ in range(full):
+            g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
+    return timed(run_steps, 1, stream) / steps
+
+
 def gemv_leg(args, steps, warmup):
     import torch
     import packed_xor_popcount_amd as bnn
@@ -151,47 +196,12 @@ def gemv_leg(args, steps, warmup):
     xring = workloads.normal(g, R, 1, K).to(torch.bfloat16).to(dev)
     xring[0].copy_(d["x"].to(dev))
     y = torch.empty((1, N), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
 
     def step(j):
         # one launch: the bf16 row is sign-packed inside the GEMV kernel
         bnn.gemv_act(xring[j], wring[j], K, bnn.EPI_SCALED, alpha=alpha, out=y)
 
-    # eager warmup, then capture R steps (one per ring entry) in a HIP graph
-    for i in range(max(warmup, 1)):
-        step(i % R)
-    torch.cuda.synchronize()
-
-    def graph_of(n):
-        gr = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream(dev)
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(gr, stream=s):
-                for j in range(n):
-                    step(j % R)
-        torch.cuda.synchronize()
-        return gr
-
-    if args.eager:  # counter collection: plain launches, no graph
-        ms_total = timed(lambda: [step(i % R) for i in range(steps)], 1, stream)
-    else:
-        full, rem = divmod(steps, R)
-        g_full = graph_of(R) if full else None
-        g_rem = graph_of(rem) if rem else None
-        for gr in (g_full, g_rem):
-            if gr is not None:
-                gr.replay()
-        torch.cuda.synchronize()
-
-        def run_steps():
-            for _ in range(full):
-                g_full.replay()
-            if g_rem is not None:
-                g_rem.replay()
-
-        ms_total = timed(run_steps, 1, stream)
-    ms_step = ms_total / steps
+    ms_step = ring_steps_ms(step, R, steps, warmup, args.eager)
     # the step is one kernel: its average duration is the step time of
     # back-to-back graph launches (an upper bound: it includes launch gaps)
     ms_gemv = ms_step
@@ -215,6 +225,83 @@ def gemv_leg(args, steps, warmup):
                   "algorithmic_bytes_per_launch": bytes_gemv},
         step_inputs=(d, N, K),
     )
+
+
+def signw_gemv_leg(steps, warmup, ring=256, eager=False):
+    """Batch-1 product of a real bf16 activation row with packed sign weights
+    (bnn_gemm_signw_bf16, GEMV kernel) on the gemv_4096 inputs: x is used
+    as is (not sign-projected), W is the same packed 4096 x 4096 matrix, with
+    the same weight ring and HIP-graph replay as the binary GEMV step."""
+    import torch
+    import packed_xor_popcount_amd as bnn
+    import workloads
+    dev = torch.device("cuda:0")
+    d = workloads.make("gemv_4096")
+    K = d["K"]
+    kw = bnn.words(K)
+    wp = bnn.pack_signs(d["w"].to(dev))
+    alpha = d["alpha"].to(dev)
+    N = wp.shape[0]
+    R = ring
+    wring = wp.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    del wp
+    g = workloads.generator(2003)
+    xring = workloads.normal(g, R, 1, K).to(torch.bfloat16).to(dev)
+    xring[0].copy_(d["x"].to(dev))
+    y = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    def step(j):
+        bnn.gemm_signw_bf16(xring[j], wring[j], K, alpha, bnn.ALGO_GEMV, out=y)
+
+    ms = ring_steps_ms(step, R, steps, warmup, eager)
+    nbytes = N * kw * 8 + K * 2 + N * 4 + N * 4  # Wp + x bf16 + alpha + y
+    ach = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "signw_gemv_4096", "value": ach, "unit": "GB/s", "ms_per_step": ms,
+            "config": {"M": 1, "K": K, "N": N, "x_dtype": "bf16 (real-valued)",
+                       "w_dtype": "packed signs", "epilogue": "alpha-scaled fp32",
+                       "weight_ring": R, "hip_graph": not eager},
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "gemv_signw_kernel", "kernel_avg_us": ms * 1e3,
+                         "algorithmic_bytes_per_launch": nbytes}}
+
+
+def signw_gemm_leg(steps, warmup):
+    """Real bf16 activations (16384 x 1024) times packed sign weights
+    (1024 x 1024), alpha-scaled fp32 output: the largest packed-kernel shape
+    of the binary_nn README's "Triton Kernel Benchmark" section."""
+    import torch
+    import packed_xor_popcount_amd as bnn
+    import workloads
+    dev = torch.device("cuda:0")
+    d = workloads.make("signw_16384")
+    M, K = d["x"].shape
+    x = d["x"].to(dev)
+    wp = bnn.pack_signs(d["w"].to(dev))
+    alpha = d["alpha"].to(dev)
+    N = wp.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        bnn.gemm_signw_bf16(x, wp, K, alpha, bnn.ALGO_AUTO, out=y)
+
+    for _ in range(max(warmup, 1)):
+        step()
+    ms = timed(step, steps, stream)
+    flops = 2.0 * M * N * K
+    nbytes = M * K * 2 + N * bnn.words(K) * 8 + N * 4 + M * N * 4
+    ach = flops / (ms * 1e-3)
+    return {"workload": "signw_16384", "value": ach / 1e12, "unit": "TFLOP/s",
+            "ms_per_step": ms,
+            "config": {"M": M, "K": K, "N": N, "x_dtype": "bf16 (real-valued)",
+                       "w_dtype": "packed signs", "epilogue": "alpha-scaled fp32"},
+            "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                         "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK, "traffic": None,
+                         "kernel": "gemm_signw_kernel (bf16 MFMA)", "kernel_avg_us": ms * 1e3,
+                         "algorithmic_flops_per_launch": flops,
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def ffn_leg(steps, warmup):
@@ -393,7 +480,8 @@ def main():
         log(f"[bench] copied {args.calibrate_copy} MiB x 8")
         return
 
-    defaults = {"gemv_4096": (1024, 64), "ffn_4096": (20, 3), "chain_65536": (50, 5)}
+    defaults = {"gemv_4096": (1024, 64), "ffn_4096": (20, 3), "chain_65536": (50, 5),
+                "signw_gemv_4096": (1024, 64), "signw_16384": (50, 5)}
     steps = args.steps if args.steps is not None else defaults[args.workload][0]
     warmup = args.warmup if args.warmup is not None else defaults[args.workload][1]
     log(f"[bench] workload={args.workload} steps={steps} warmup={warmup}")
@@ -401,8 +489,12 @@ def main():
         res = gemv_leg(args, steps, warmup)
     elif args.workload == "ffn_4096":
         res = ffn_leg(steps, warmup)
-    else:
+    elif args.workload == "chain_65536":
         res = chain_leg(steps, warmup)
+    else:
+        leg = (signw_gemv_leg(steps, warmup, args.ring, args.eager)
+               if args.workload == "signw_gemv_4096" else signw_gemm_leg(steps, warmup))
+        res = dict(leg, config=dict(leg["config"], workload=leg["workload"]), step_inputs=None)
     log(f"[bench] {args.workload}: {res['value']:.1f} {res['unit']}, "
         f"{res['ms_per_step'] * 1e3:.2f} us/step")
 
@@ -423,7 +515,15 @@ def main():
         out["secondary"] = {"workload": "ffn_4096", "value": sec["value"], "unit": sec["unit"],
                             "ms_per_step": sec["ms_per_step"], "roofline": sec["roofline"],
                             "ablation": sec["ablation"]}
-    if not args.no_cpu_baseline:
+    if args.workload == "gemv_4096" and not args.no_secondary and not args.rows:
+        # the real-activation product (packed sign weights), both regimes
+        out["signw"] = []
+        for leg in (signw_gemv_leg(1024, 64), signw_gemm_leg(20, 3)):
+            log(f"[bench] {leg['workload']}: {leg['value']:.1f} {leg['unit']}, "
+                f"{leg['ms_per_step'] * 1e3:.2f} us/step")
+            out["signw"].append({k: leg[k] for k in ("workload", "value", "unit", "ms_per_step",
+                                                     "config", "roofline")})
+    if not args.no_cpu_baseline and res["step_inputs"] is not None:
         log("[bench] timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(args.workload, res["step_inputs"], args.cpu_seconds)
     print(json.dumps(out), flush=True)

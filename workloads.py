@@ -26,6 +26,11 @@ Workload shapes (seed = 1000 + index):
   5 chain_65536  M=65536, 512 -> 256 -> 128 -> 64, all ~ N(0,1) fp32; hidden
                                            layers sign -> repack, last layer
                                            alpha-scaled fp32
+  6 signw_16384  M=16384, K=1024, N=1024,  X ~ N(0,1) bf16 kept real-valued,
+                                           W ~ N(0,1) fp32 (sign-packed),
+                                           alpha-scaled fp32 out: the largest
+                                           packed-kernel shape of the binary_nn
+                                           README ("Triton Kernel Benchmark")
 """
 from __future__ import annotations
 
@@ -37,6 +42,7 @@ WORKLOADS = {
     "edge_1000": dict(index=3, M=64, K=1000, N=1000),
     "ffn_4096": dict(index=4, M=4096, K=4096, N=11008),
     "chain_65536": dict(index=5, M=65536, dims=(512, 256, 128, 64)),
+    "signw_16384": dict(index=6, M=16384, K=1024, N=1024),
 }
 
 
@@ -106,6 +112,10 @@ def make(name: str) -> dict:
         x = normal(g, spec["M"], dims[0])
         ws = [normal(g, dims[i + 1], dims[i]) for i in range(len(dims) - 1)]
         return dict(x=x, weights=ws, alpha=absmean_alpha(ws[-1]), dims=dims)
+    if name == "signw_16384":
+        x = normal(g, 16384, 1024).to(torch.bfloat16)
+        w = normal(g, 1024, 1024)
+        return dict(x=x, w=w, alpha=absmean_alpha(w), K=1024)
     raise KeyError(name)
 
 
