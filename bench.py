@@ -17,8 +17,12 @@ synthetic input, inputs already resident in HBM:
   ffn_4096: pack X (4096 x 4096 bf16) and run the alpha-scaled GEMM against
       packed W (11008 x 4096).  value = binary GOPS (2*M*N*K / s).
   chain_65536: pack X (65536 x 512 fp32), two sign->repack layers
-      (512->256->128) and an alpha-scaled last layer (128->64).
+      (512->256->128) and an alpha-scaled last layer (128->64), as one
+      bnn_chain3 launch (the four separate launches are timed beside it).
       value = binary GOPS over the three layers.
+  signw_gemv_4096 / signw_16384: real bf16 activations times packed sign
+      weights (bnn_gemm_signw_bf16), batch-1 and 16384 x 1024 x 1024; both
+      also appear in the default record under "signw".
 
 "roofline" reports the dominant kernel of the step: its algorithmic bytes
 (or binary ops) per launch divided by its average duration, measured here
@@ -128,7 +132,7 @@ def recorded_traffic(profile_name, sources):
 
 
 GEMV_SOURCES = ["gemv.hip", "sign_bits.h", "bnn_internal.h"]
-MFMA_SOURCES = ["gemm_mfma.hip", "bnn_internal.h"]
+MFMA_SOURCES = ["gemm_mfma.hip", "fp4_ops.h", "bnn_internal.h"]
 
 
 def ring_steps_ms(step, R, steps, warmup, eager):
@@ -373,24 +377,34 @@ def chain_leg(steps, warmup):
         bnn.gemm_sign_repack(h1, wps[1], dims[1], out=h2)
         bnn.gemm_u64_scaled(h2, wps[2], alpha, dims[2], out=y)
 
-    def layer1():
-        bnn.gemm_sign_repack(h0, wps[0], dims[0], out=h1)
+    def fused():
+        # the same step in one launch: pack, two repack layers and the scaled
+        # layer with the packed hidden rows kept on chip (bit-identical)
+        bnn.chain3(x, wps[0], wps[1], wps[2], alpha, out=y)
 
     for _ in range(max(warmup, 1)):
         step()
-    ms_step = timed(step, steps, stream)
-    ms_l1 = timed(layer1, steps, stream)
+        fused()
+    ms_sep = timed(step, steps, stream)
+    ms_step = timed(fused, steps, stream)
     ops = sum(2.0 * M * dims[i] * dims[i + 1] for i in range(3))
-    ops1 = 2.0 * M * dims[0] * dims[1]
+    # HBM bytes of the fused launch: the fp32 input, the fp32 output, the
+    # packed weights and the scales
+    nbytes = (M * dims[0] * 4 + M * dims[3] * 4 + sum(w.numel() * 8 for w in wps)
+              + dims[3] * 4)
+    ach = nbytes / (ms_step * 1e-3) / 1e9
     return dict(
         value=ops / (ms_step * 1e-3) / 1e9, unit="binary GOPS", ms_per_step=ms_step,
         config={"workload": "chain_65536", "M": M, "dims": list(dims), "x_dtype": "fp32",
-                "hidden": "sign->repack u64", "epilogue": "alpha-scaled fp32"},
-        roofline={"bound": "mfma", "achieved": ops1 / (ms_l1 * 1e-3) / 1e12,
-                  "peak": MFMA_FP4_PEAK_OPS / 1e12, "unit": "T binary-ops/s (= FP4 TFLOP/s)",
-                  "frac": ops1 / (ms_l1 * 1e-3) / MFMA_FP4_PEAK_OPS, "traffic": None,
-                  "kernel": "gemm_mfma_kernel (sign->repack, layer 1)",
-                  "kernel_avg_us": ms_l1 * 1e3, "algorithmic_ops_per_launch": ops1},
+                "hidden": "sign->repack u64", "epilogue": "alpha-scaled fp32",
+                "launch": "bnn_chain3 (fused)"},
+        roofline={"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                  "kernel": "chain3_kernel (pack + 3 layers, one launch)",
+                  "kernel_avg_us": ms_step * 1e3, "algorithmic_bytes_per_launch": nbytes,
+                  "mfma_frac": ops / (ms_step * 1e-3) / MFMA_FP4_PEAK_OPS},
+        unfused={"us_per_step": ms_sep * 1e3, "launches": 4,
+                 "value": ops / (ms_sep * 1e-3) / 1e9},
         step_inputs=(d, None, None),
     )
 
@@ -509,6 +523,8 @@ def main():
         out["binary_gops"] = res["binary_gops"]
     if "ablation" in res:
         out["ablation"] = res["ablation"]
+    if "unfused" in res:
+        out["unfused"] = res["unfused"]
     if args.workload == "gemv_4096" and not args.no_secondary and not args.rows:
         sec = ffn_leg(10, 2)
         log(f"[bench] secondary ffn_4096: {sec['value']:.1f} binary GOPS")

@@ -233,6 +233,33 @@ bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, c
                                float *y, int64_t M, int64_t N, int64_t K, int algo, void *stream);
 
 /*
+ * bnn_chain3 -- three chained binary layers in one launch: the M real-valued
+ * input rows x (fp32 or bf16, K0 columns, row stride ldx) are sign-projected
+ * and packed; layer 1 (w1: N1 x bnn_words(K0)) and layer 2 (w2: N2 x
+ * bnn_words(N1)) end in sign -> repack; layer 3 (w3: N3 x bnn_words(N2))
+ * ends in fp32, times alpha3[n] when alpha3 is non-NULL.  The result is bit
+ * for bit that of bnn_pack_signs, bnn_gemm_sign_repack (twice) and
+ * bnn_gemm_u64_scaled (or the int32 dot as fp32 when alpha3 is NULL); the
+ * packed hidden activations stay on chip.  ("Encoder / decoder",
+ * BinaryAutoEncoder, and the balanced_ternary_engine README 512 -> 256 ->
+ * 128 -> 64 stack, for chained binary layers; "Binary Math Effectiveness",
+ * section 1, for every step.)
+ *
+ *   x        M x ldx values of type dtype (BNN_FP32 / BNN_BF16), ldx >= K0,
+ *            element-aligned.
+ *   w1..w3   packed weights as above, 8-byte aligned.
+ *   alpha3   N3 fp32 scales, 4-byte aligned, or NULL.
+ *   y        M x N3 fp32 output, row-major, 4-byte aligned.
+ * Supported layer sizes: K0, N1, N2 in {128, 256, 384, 512}; N3 a multiple
+ * of 32 in [32, 512]; otherwise BNN_E_SHAPE (use the separate calls).
+ * M = 0 launches nothing.  Errors: BNN_E_DTYPE, BNN_E_SHAPE, BNN_E_NULL,
+ * BNN_E_ALIGN, BNN_E_LAUNCH.
+ */
+bnn_status bnn_chain3(const void *x, int dtype, int64_t ldx, const uint64_t *w1,
+                      const uint64_t *w2, const uint64_t *w3, const float *alpha3, float *y,
+                      int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3, void *stream);
+
+/*
  * bnn_gemm_ex -- the general form of the three products above, with an
  * explicit kernel family (see bnn_algo; the matrix-core family takes the
  * same exact integer sum of +-1 products on the MFMA units, which "Binary

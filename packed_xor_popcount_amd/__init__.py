@@ -27,8 +27,8 @@ __all__ = [
     "BnnError", "EPI_I32", "EPI_SCALED", "EPI_REPACK", "ALGO_AUTO", "ALGO_GEMV", "ALGO_TILED",
     "ALGO_MFMA",
     "library", "library_path", "words", "pack_signs", "gemm_u64", "gemm_u64_scaled",
-    "gemm_sign_repack", "gemm_sign_repack_thr", "flip_words", "gemm_signw_bf16", "gemm_ex",
-    "gemv_act", "version",
+    "gemm_sign_repack", "gemm_sign_repack_thr", "flip_words", "gemm_signw_bf16", "chain3",
+    "gemm_ex", "gemv_act", "version",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +40,7 @@ ALGO_AUTO, ALGO_GEMV, ALGO_TILED, ALGO_MFMA = 0, 1, 2, 3
 
 EXPORTED = ("bnn_words", "bnn_status_str", "bnn_version", "bnn_pack_signs", "bnn_gemm_u64",
             "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack", "bnn_gemm_ex", "bnn_gemv_act",
-            "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16")
+            "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16", "bnn_chain3")
 
 
 class BnnError(RuntimeError):
@@ -75,8 +75,10 @@ def library():
     lib.bnn_gemv_act.argtypes = [P, I, I64, P, P, P, I64, I64, I64, I, P]
     lib.bnn_gemm_sign_repack_thr.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     lib.bnn_gemm_signw_bf16.argtypes = [P, I64, P, P, P, I64, I64, I64, I, P]
+    lib.bnn_chain3.argtypes = [P, I, I64, P, P, P, P, P, I64, I64, I64, I64, I64, P]
     for name in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack",
-                 "bnn_gemm_ex", "bnn_gemv_act", "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16"):
+                 "bnn_gemm_ex", "bnn_gemv_act", "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16",
+                 "bnn_chain3"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -290,4 +292,36 @@ def gemm_signw_bf16(x, wp, K=None, alpha=None, algo=ALGO_AUTO, out=None):
     st = library().bnn_gemm_signw_bf16(_ptr(x), ldx, _ptr(wp), _ptr(alpha), _ptr(out), M, N, K,
                                        int(algo), _stream(x))
     _check(st, "bnn_gemm_signw_bf16")
+    return out
+
+
+def chain3(x, w1, w2, w3, alpha3=None, out=None):
+    """fp32 ``(M, N3)``: three chained binary layers in one launch
+    (bnn_chain3).  ``x`` is a 2-D fp32 or bf16 CUDA tensor (unit stride along
+    its last dimension, K0 columns); ``w1``, ``w2``, ``w3`` are packed weights
+    ``(N1, words(K0))``, ``(N2, words(N1))``, ``(N3, words(N2))``; ``alpha3`` is
+    None or a contiguous float32 ``(N3,)``.  Equal, bit for bit, to pack_signs
+    -> gemm_sign_repack -> gemm_sign_repack -> gemm_u64_scaled."""
+    _need_cuda("x", x)
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D with unit stride along its last dimension")
+    if x.dtype == torch.float32:
+        dt = BNN_FP32
+    elif x.dtype == torch.bfloat16:
+        dt = BNN_BF16
+    else:
+        raise TypeError("x must be float32 or bfloat16")
+    M, K0 = x.shape
+    N1 = _packed("w1", w1, K0)
+    N2 = _packed("w2", w2, N1)
+    N3 = _packed("w3", w3, N2)
+    if alpha3 is not None:
+        _need_cuda("alpha3", alpha3)
+        if alpha3.dtype != torch.float32 or alpha3.shape != (N3,) or not alpha3.is_contiguous():
+            raise ValueError("alpha3 must be a contiguous float32 tensor of shape (N3,)")
+    out = _out_for(EPI_SCALED, M, N3, x.device, out)
+    ldx = x.stride(0) if M > 1 else max(K0, 1)
+    st = library().bnn_chain3(_ptr(x), dt, ldx, _ptr(w1), _ptr(w2), _ptr(w3), _ptr(alpha3),
+                              _ptr(out), M, K0, N1, N2, N3, _stream(x))
+    _check(st, "bnn_chain3")
     return out

@@ -64,6 +64,16 @@ hipError_t launch_signw_mfma(const uint16_t *x, int64_t ldx, const uint64_t *wp,
                              const float *alpha, float *y, int64_t M, int64_t N, int64_t K,
                              hipStream_t s);
 
+// Three chained binary layers in one launch (bnn_chain3): pack real rows
+// (dtype 0 fp32, 1 bf16), two sign -> repack layers, one fp32 layer.  The
+// packed weights of all three layers and each wave's hidden rows live in
+// LDS, at most this many bytes.
+constexpr int64_t kChain3MaxLds = 64 * 1024;
+bool chain3_dims_ok(int64_t K0, int64_t N1, int64_t N2, int64_t N3);
+hipError_t launch_chain3(const void *x, int dtype, int64_t ldx, const uint64_t *w1,
+                         const uint64_t *w2, const uint64_t *w3, const float *alpha, float *y,
+                         int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3, hipStream_t s);
+
 // Threshold-repack operands, loaded by the kernels before their K loops from
 // clamped (always in-bounds) indexes: the threshold of output column n, and
 // the flip word of 64-column group wi with its bits past column N cleared

@@ -170,3 +170,23 @@ def test_signw_validation(lib):
     assert f(FAKE, 64, FAKE, P(0x1002), FAKE, 1, 1, 64, 0, None) == E_ALIGN  # alpha
     assert f(FAKE, 64, FAKE, None, P(0x1002), 1, 1, 64, 0, None) == E_ALIGN  # y
     assert f(None, 64, FAKE, None, None, 0, 3, 64, 0, None) == OK            # empty
+
+
+def test_chain3_validation(lib):
+    f = lib.bnn_chain3
+    # (x, dtype, ldx, w1, w2, w3, alpha3, y, M, K0, N1, N2, N3, stream)
+    ok_dims = (512, 256, 128, 64)
+    assert f(FAKE, 7, 512, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None) == E_DTYPE
+    for dims in [(500, 256, 128, 64), (640, 256, 128, 64), (512, 192, 128, 64),
+                 (512, 256, 64, 64), (512, 256, 128, 48), (512, 256, 128, 544),
+                 (512, 512, 512, 512)]:   # the last: weights too large for LDS
+        assert f(FAKE, 0, 1024, FAKE, FAKE, FAKE, None, FAKE, 4, *dims, None) == E_SHAPE, dims
+    assert f(FAKE, 0, 511, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None) == E_SHAPE  # ldx < K0
+    assert f(FAKE, 0, 512, FAKE, FAKE, FAKE, None, FAKE, -1, *ok_dims, None) == E_SHAPE
+    assert f(None, 0, 512, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None) == E_NULL
+    assert f(FAKE, 0, 512, FAKE, None, FAKE, None, FAKE, 4, *ok_dims, None) == E_NULL
+    assert f(FAKE, 0, 512, FAKE, FAKE, FAKE, None, None, 4, *ok_dims, None) == E_NULL
+    assert f(P(0x1002), 0, 512, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None) == E_ALIGN
+    assert f(FAKE, 0, 512, FAKE, FAKE, FAKE_ODD, None, FAKE, 4, *ok_dims, None) == E_ALIGN
+    assert f(FAKE, 0, 512, FAKE, FAKE, FAKE, P(0x1001), FAKE, 4, *ok_dims, None) == E_ALIGN
+    assert f(None, 1, 512, FAKE, FAKE, FAKE, None, None, 0, *ok_dims, None) == OK     # M = 0
