@@ -27,7 +27,8 @@
 //    v_dot2_f32_bf16 against the activation pair held in LDS; the L partial
 //    sums are combined with DPP moves.
 //  * gemm_signw_kernel (larger M, matrix cores): v_mfma_f32_32x32x16_bf16
-//    with the activation tile staged in LDS (pair order) and the weight
+//    with the activation tile staged in LDS (pair order, two tiles, one
+//    barrier per step) from buffer loads two steps ahead, and the weight
 //    fragments unpacked in registers from the packed words, which every lane
 //    loads straight from L2.  Blocks are mapped so that the tiles of one
 //    8th of the rows run on one XCD (its L2 then reads those rows once).
@@ -222,17 +223,19 @@ __global__ void __launch_bounds__(256)
 constexpr int kBK = 64;                       // elements of K per block step (one W word)
 constexpr int kARowBytes = 2 * 64 + 16;       // two chunks of 64 B + pad
 
-template <int WR, int WC, int RB, int CB, bool SCALED, bool XV8>
-__global__ void __launch_bounds__(256)
+// MINB: blocks per CU the register allocation must allow.
+template <int WR, int WC, int RB, int CB, int MINB, bool SCALED, bool XV8>
+__global__ void __launch_bounds__(256, MINB)
     gemm_signw_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint64_t *__restrict__ wp,
                       const float *__restrict__ alpha, float *__restrict__ y, int M, int N, int K,
                       int kw, int tiles_m, int tiles_n) {
   static_assert(WR * WC == 4, "4 waves per block");
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
-  constexpr int kPieces = BM * 8;            // 16-byte A fragments per block step
-  static_assert(kPieces % 256 == 0, "whole fragments per thread");
-  constexpr int kPerThread = kPieces / 256;
-  __shared__ __attribute__((aligned(16))) unsigned char as[BM * kARowBytes];
+  constexpr int kPerThread = BM * 8 / 256;  // 16-byte A fragments staged per thread per step
+  static_assert(BM * 8 % 256 == 0, "whole fragments per thread");
+  // Two LDS tiles: step s is staged into tile s % 2 while the other one may
+  // still be read by step s - 1, so one barrier per step suffices.
+  __shared__ __attribute__((aligned(16))) unsigned char as[2][BM * kARowBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -242,17 +245,17 @@ __global__ void __launch_bounds__(256)
 
   // XCD-aware tile order: hardware places block b on XCD b % 8, so block b
   // takes logical tile (b % 8) * per + b / 8 and each XCD owns a contiguous
-  // range of tiles (rows of X are then fetched by one L2).
+  // range of tiles (rows of X are then fetched by one L2).  Grids that are
+  // not a multiple of 8 keep the plain order.
   const int nblocks = tiles_m * tiles_n;
-  const int per = (nblocks + 7) >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  // Grids that are not a multiple of 8 fall back to the plain order.
-  const int tile = (nblocks % 8 == 0) ? xcd * per + slot : (int)blockIdx.x;
+  const int per = nblocks >> 3;
+  const int tile = (nblocks % 8 == 0) ? (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3)
+                                      : (int)blockIdx.x;
   const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
   const int m0 = tm * BM + (wave / WC) * (RB * 32);
   const int n0 = tn * BN + (wave % WC) * (CB * 32);
 
-  // Weight words of this lane's columns (clamped; columns past N are never stored).
+  // Weight rows of this lane's columns (clamped; columns past N are never stored).
   const uint64_t *bcol[CB];
   float a_pre[CB];
 #pragma unroll
@@ -263,40 +266,72 @@ __global__ void __launch_bounds__(256)
     a_pre[cb] = SCALED ? alpha[n] : 1.0f;
   }
 
-  // A fragment pieces staged by this thread: fragment f = tid + 256 i is
-  // (row f / 8, chunk (f / 4) & 1, t = (f / 2) & 1, h = f & 1); it holds the
-  // four pairs (x[b + j], x[b + j + 16]), b = 32 chunk + 8t + 4h.
-  const int64_t row_lim = M - 1;
-  auto load_a = [&](int kb, uint32_t (&lo)[kPerThread][2], uint32_t (&hi)[kPerThread][2]) {
+  // Fragments staged by this thread: f = tid + 256 i is (row f / 8, chunk
+  // (f / 4) & 1, t = (f / 2) & 1, h = f & 1) and holds the four pairs
+  // (x[b + j], x[b + j + 16]), b = 32 chunk + 8t + 4h.  f % 8 = tid % 8 for
+  // every i, so all of a thread's fragments share the offset b and their rows
+  // are 32 apart.  Full steps (all 64 elements inside K) read two 8-byte
+  // pieces per fragment through a buffer resource: the per-thread byte
+  // offset is fixed and the step's offset is a scalar, so a step costs no
+  // vector address arithmetic.  The last, partial step (K % 64 != 0) reads
+  // element by element with zero fill past K.
+  const int koff = 32 * ((tid >> 2) & 1) + 8 * ((tid >> 1) & 1) + 4 * (tid & 1);
+  const int frow = tid >> 3;
+  int64_t xrow[kPerThread];
+  uint32_t voff[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    int64_t m = (int64_t)tm * BM + frow + 32 * i;
+    m = m < M - 1 ? m : M - 1;
+    xrow[i] = m * ldx + koff;
+    voff[i] = (uint32_t)(xrow[i] * 2);
+  }
+  typedef uint32_t Stage[kPerThread][4];  // lo pair, hi pair of each fragment
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x), (short)0, 0x7FFFFFFF, 0x00020000);
+  auto load_full = [&](int kb, Stage &r) {
+    const int soff = kb * kBK * 2;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int f = tid + 256 * i;
-      int64_t m = (int64_t)tm * BM + (f >> 3);
-      m = m < row_lim ? m : row_lim;
-      const int64_t k = (int64_t)kb * kBK + 32 * ((f >> 2) & 1) + 8 * ((f >> 1) & 1) + 4 * (f & 1);
-      if (XV8 && k + 20 <= K) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(x + m * ldx + k);
-        const uint2 b = *reinterpret_cast<const uint2 *>(x + m * ldx + k + 16);
-        lo[i][0] = a.x; lo[i][1] = a.y;
-        hi[i][0] = b.x; hi[i][1] = b.y;
+      if (XV8) {
+        const v2u a = __builtin_amdgcn_raw_buffer_load_b64(xres, voff[i], soff, 0);
+        const v2u b = __builtin_amdgcn_raw_buffer_load_b64(xres, voff[i] + 32, soff, 0);
+        r[i][0] = a.x; r[i][1] = a.y; r[i][2] = b.x; r[i][3] = b.y;
       } else {
-        lo[i][0] = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 1, K) << 16);
-        lo[i][1] = x_at(x, ldx, m, k + 2, K) | (x_at(x, ldx, m, k + 3, K) << 16);
-        hi[i][0] = x_at(x, ldx, m, k + 16, K) | (x_at(x, ldx, m, k + 17, K) << 16);
-        hi[i][1] = x_at(x, ldx, m, k + 18, K) | (x_at(x, ldx, m, k + 19, K) << 16);
+        const uint16_t *p = x + xrow[i] + (int64_t)kb * kBK;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          r[i][j] = (uint32_t)p[2 * j] | ((uint32_t)p[2 * j + 1] << 16);
+          r[i][2 + j] = (uint32_t)p[16 + 2 * j] | ((uint32_t)p[16 + 2 * j + 1] << 16);
+        }
       }
     }
   };
-  auto store_a = [&](const uint32_t (&lo)[kPerThread][2], const uint32_t (&hi)[kPerThread][2]) {
+  auto load_tail = [&](int kb, Stage &r) {
+    const int64_t k0 = (int64_t)kb * kBK + koff;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int f = tid + 256 * i;
-      uint4 v;  // pairs j = 0..3: low half from lo, high half from hi
-      v.x = __builtin_amdgcn_perm(hi[i][0], lo[i][0], 0x05040100u);
-      v.y = __builtin_amdgcn_perm(hi[i][0], lo[i][0], 0x07060302u);
-      v.z = __builtin_amdgcn_perm(hi[i][1], lo[i][1], 0x05040100u);
-      v.w = __builtin_amdgcn_perm(hi[i][1], lo[i][1], 0x07060302u);
-      *reinterpret_cast<uint4 *>(as + (f >> 3) * kARowBytes + (f & 7) * 16) = v;
+      const uint16_t *p = x + xrow[i] + (int64_t)kb * kBK;
+      uint32_t e[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = k0 + j < K ? (uint32_t)p[j] : 0u;
+        e[4 + j] = k0 + 16 + j < K ? (uint32_t)p[16 + j] : 0u;
+      }
+      r[i][0] = e[0] | (e[1] << 16); r[i][1] = e[2] | (e[3] << 16);
+      r[i][2] = e[4] | (e[5] << 16); r[i][3] = e[6] | (e[7] << 16);
+    }
+  };
+  auto store_a = [&](const Stage &r, unsigned char *buf) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      uint4 v;  // pairs j = 0..3: low half from the first piece, high half from the second
+      v.x = __builtin_amdgcn_perm(r[i][2], r[i][0], 0x05040100u);
+      v.y = __builtin_amdgcn_perm(r[i][2], r[i][0], 0x07060302u);
+      v.z = __builtin_amdgcn_perm(r[i][3], r[i][1], 0x05040100u);
+      v.w = __builtin_amdgcn_perm(r[i][3], r[i][1], 0x07060302u);
+      *reinterpret_cast<uint4 *>(buf + (frow + 32 * i) * kARowBytes + (tid & 7) * 16) = v;
     }
   };
 
@@ -308,27 +343,9 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  const int nsteps = (K + kBK - 1) / kBK;  // == kw
   const uint32_t mask = kSignMask, ones = kPlusOnes;
   const int wrow = (wave / WC) * (RB * 32);  // this wave's first row inside the block tile
-
-  uint32_t lo[kPerThread][2], hi[kPerThread][2];
-  uint64_t wcur[CB];
-  if (nsteps > 0) {
-    load_a(0, lo, hi);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wcur[cb] = bcol[cb][0];
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    store_a(lo, hi);
-    __syncthreads();
-    // prefetch the next step (clamped to the last one: in bounds, unused)
-    const int sn = s + 1 < nsteps ? s + 1 : s;
-    uint64_t wnext[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wnext[cb] = bcol[cb][sn];
-    load_a(sn, lo, hi);
-
+  auto compute = [&](const unsigned char *buf, const uint64_t (&wcur)[CB]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       // weight chunk q of each column, pre-shifted by 4 for lane half 0
@@ -351,7 +368,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           const uint4 av = *reinterpret_cast<const uint4 *>(
-              as + (wrow + rb * 32 + li) * kARowBytes + q * 64 + t * 32 + h * 16);
+              buf + (wrow + rb * 32 + li) * kARowBytes + q * 64 + t * 32 + h * 16);
           const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
@@ -359,9 +376,54 @@ __global__ void __launch_bounds__(256)
         }
       }
     }
+  };
+
+  // Two register stages in flight over the full steps: while step s is
+  // staged and computed, the activation loads of step s + 2 are in flight.
+  // The loop is unrolled by two so that each stage keeps its own registers,
+  // and no loaded value is ever copied (a copy waits for its load): a stage's
+  // activation registers are reloaded right after they are written to LDS,
+  // its weight words right after the step that used them.  Loads past the
+  // last full step re-read it (in bounds, unused).
+  const int nfull = K / kBK;
+  const int last = nfull - 1;
+  Stage ra, rb;
+  uint64_t wa[CB], wb[CB];
+  if (nfull > 0) {
+    load_full(0, ra);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wcur[cb] = wnext[cb];
-    __syncthreads();  // the tile is consumed before the next store
+    for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][0];
+    const int s1 = last < 1 ? last : 1;
+    load_full(s1, rb);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wb[cb] = bcol[cb][s1];
+  }
+  for (int s = 0; s < nfull; s += 2) {
+    const int s2 = s + 2 < last ? s + 2 : last;
+    store_a(ra, as[0]);
+    __syncthreads();
+    load_full(s2, ra);
+    compute(as[0], wa);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][s2];
+    if (s + 1 < nfull) {
+      const int s3 = s + 3 < last ? s + 3 : last;
+      store_a(rb, as[1]);
+      __syncthreads();
+      load_full(s3, rb);
+      compute(as[1], wb);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) wb[cb] = bcol[cb][s3];
+    }
+  }
+  if (nfull < kw) {  // the partial last step, zero past K (uniform branch)
+    load_tail(nfull, ra);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][nfull];
+    __syncthreads();  // both tiles are free
+    store_a(ra, as[0]);
+    __syncthreads();
+    compute(as[0], wa);
   }
 
   const int64_t ld = N;
@@ -410,14 +472,14 @@ hipError_t launch_gemv_vec(const uint16_t *x, int64_t ldx, const uint64_t *wp, c
 #undef BNN_SIGNW_L
 }
 
-template <bool SCALED, bool XV8>
+template <int RB, int CB, int MINB, bool SCALED, bool XV8>
 hipError_t launch_mfma_cfg(const uint16_t *x, int64_t ldx, const uint64_t *wp, const float *alpha,
                            float *y, int M, int N, int K, hipStream_t s) {
-  constexpr int WR = 2, WC = 2, RB = 2, CB = 2;
+  constexpr int WR = 2, WC = 2;
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
   const int kw = (K + 63) / 64;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_signw_kernel<WR, WC, RB, CB, SCALED, XV8>),
+  hipLaunchKernelGGL((gemm_signw_kernel<WR, WC, RB, CB, MINB, SCALED, XV8>),
                      dim3((unsigned)(tiles_m * tiles_n)), dim3(256), 0, s, x, ldx, wp, alpha, y, M,
                      N, K, kw, tiles_m, tiles_n);
   return hipGetLastError();
@@ -451,14 +513,25 @@ hipError_t launch_signw_gemv(const uint16_t *x, int64_t ldx, const uint64_t *wp,
 hipError_t launch_signw_mfma(const uint16_t *x, int64_t ldx, const uint64_t *wp,
                              const float *alpha, float *y, int64_t M, int64_t N, int64_t K,
                              hipStream_t s) {
-  // 8-byte activation loads need 8-byte aligned row starts.
-  const bool xv8 = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0 || M == 1);
-  if (alpha) {
-    return xv8 ? launch_mfma_cfg<true, true>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s)
-               : launch_mfma_cfg<true, false>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s);
+  // 8-byte activation loads need 8-byte aligned row starts, and the buffer
+  // loads 32-bit byte offsets (all of X below 2 GiB).
+  const bool xv8 = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0 || M == 1) &&
+                   ((M - 1) * ldx + K) * 2 < (int64_t(1) << 31);
+  // Wide outputs: 128 x 256 block tiles (2 x 4 tiles of 32 x 32 per wave,
+  // two blocks per CU); narrow ones: 128 x 128.
+  const int m = (int)M, n = (int)N, k = (int)K;
+  if (N >= 256) {
+    if (alpha)
+      return xv8 ? launch_mfma_cfg<2, 4, 2, true, true>(x, ldx, wp, alpha, y, m, n, k, s)
+                 : launch_mfma_cfg<2, 4, 2, true, false>(x, ldx, wp, alpha, y, m, n, k, s);
+    return xv8 ? launch_mfma_cfg<2, 4, 2, false, true>(x, ldx, wp, alpha, y, m, n, k, s)
+               : launch_mfma_cfg<2, 4, 2, false, false>(x, ldx, wp, alpha, y, m, n, k, s);
   }
-  return xv8 ? launch_mfma_cfg<false, true>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s)
-             : launch_mfma_cfg<false, false>(x, ldx, wp, alpha, y, (int)M, (int)N, (int)K, s);
+  if (alpha)
+    return xv8 ? launch_mfma_cfg<2, 2, 1, true, true>(x, ldx, wp, alpha, y, m, n, k, s)
+               : launch_mfma_cfg<2, 2, 1, true, false>(x, ldx, wp, alpha, y, m, n, k, s);
+  return xv8 ? launch_mfma_cfg<2, 2, 1, false, true>(x, ldx, wp, alpha, y, m, n, k, s)
+             : launch_mfma_cfg<2, 2, 1, false, false>(x, ldx, wp, alpha, y, m, n, k, s);
 }
 
 }  // namespace bnn
