@@ -46,6 +46,9 @@ namespace {
 #ifndef BNN_MFMA_SW
 #define BNN_MFMA_SW 8  // words of K per register step
 #endif
+#ifndef BNN_MFMA_PIN
+#define BNN_MFMA_PIN 1  // pin each step's prefetch ahead of the step's MFMAs
+#endif
 #ifndef BNN_MFMA_SCHED
 #define BNN_MFMA_SCHED 0  // VALU ops to interleave after each MFMA (0: compiler's choice)
 #endif
@@ -177,7 +180,9 @@ __global__ void __launch_bounds__(256)
   };
 
   // Two register buffers in ping-pong: the loads of step s+1 are in flight
-  // while step s runs.  Both halves of the pair loop are unconditional (a
+  // while step s runs.  A scheduling barrier keeps each prefetch ahead of the
+  // MFMAs it is meant to overlap (left alone, the scheduler sinks the loads
+  // behind most of the step, and the loop head then waits for every load).  Both halves of the pair loop are unconditional (a
   // conditional use would let the compiler sink the prefetch behind the
   // MFMAs); the load past the last clean step re-reads that step (clamped,
   // in bounds, unused).  An odd last step runs after the loop.
@@ -187,8 +192,14 @@ __global__ void __launch_bounds__(256)
   int s = 0;
   for (; s + 1 < nclean; s += 2) {
     load_clean(s + 1, a1, b1);
+#if BNN_MFMA_PIN
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the MFMAs
+#endif
     mma_step(a0, b0, false, s);
     load_clean(s + 2 < nclean ? s + 2 : nclean - 1, a0, b0);
+#if BNN_MFMA_PIN
+    __builtin_amdgcn_sched_barrier(0);
+#endif
     mma_step(a1, b1, false, s + 1);
   }
   if (s < nclean) mma_step(a0, b0, false, s);

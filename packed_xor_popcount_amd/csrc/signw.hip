@@ -223,6 +223,9 @@ __global__ void __launch_bounds__(256)
 constexpr int kBK = 64;                       // elements of K per block step (one W word)
 constexpr int kARowBytes = 2 * 64 + 16;       // two chunks of 64 B + pad
 
+#ifndef BNN_SIGNW_PIN
+#define BNN_SIGNW_PIN 1  // keep each step's prefetch ahead of its MFMAs
+#endif
 // MINB: blocks per CU the register allocation must allow.
 template <int WR, int WC, int RB, int CB, int MINB, bool SCALED, bool XV8>
 __global__ void __launch_bounds__(256, MINB)
@@ -403,6 +406,9 @@ __global__ void __launch_bounds__(256, MINB)
     store_a(ra, as[0]);
     __syncthreads();
     load_full(s2, ra);
+#if BNN_SIGNW_PIN
+    __builtin_amdgcn_sched_barrier(0);
+#endif
     compute(as[0], wa);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][s2];
@@ -411,6 +417,9 @@ __global__ void __launch_bounds__(256, MINB)
       store_a(rb, as[1]);
       __syncthreads();
       load_full(s3, rb);
+#if BNN_SIGNW_PIN
+      __builtin_amdgcn_sched_barrier(0);
+#endif
       compute(as[1], wb);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) wb[cb] = bcol[cb][s3];
