@@ -133,6 +133,8 @@ def recorded_traffic(profile_name, sources):
 
 GEMV_SOURCES = ["gemv.hip", "sign_bits.h", "bnn_internal.h"]
 MFMA_SOURCES = ["gemm_mfma.hip", "fp4_ops.h", "bnn_internal.h"]
+CHAIN_SOURCES = ["chain.hip", "fp4_ops.h", "sign_bits.h", "bnn_internal.h"]
+SIGNW_SOURCES = ["signw.hip", "bnn_internal.h"]
 
 
 def ring_steps_ms(step, R, steps, warmup, eager):
@@ -265,7 +267,8 @@ def signw_gemv_leg(steps, warmup, ring=256, eager=False):
                        "w_dtype": "packed signs", "epilogue": "alpha-scaled fp32",
                        "weight_ring": R, "hip_graph": not eager},
             "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                         "frac": ach / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic("signw_gemv_4096_traffic.md", SIGNW_SOURCES),
                          "kernel": "gemv_signw_kernel", "kernel_avg_us": ms * 1e3,
                          "algorithmic_bytes_per_launch": nbytes}}
 
@@ -301,7 +304,8 @@ def signw_gemm_leg(steps, warmup):
             "config": {"M": M, "K": K, "N": N, "x_dtype": "bf16 (real-valued)",
                        "w_dtype": "packed signs", "epilogue": "alpha-scaled fp32"},
             "roofline": {"bound": "mfma", "achieved": ach / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
-                         "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK, "traffic": None,
+                         "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK,
+                         "traffic": recorded_traffic("signw_16384_traffic.md", SIGNW_SOURCES),
                          "kernel": "gemm_signw_kernel (bf16 MFMA)", "kernel_avg_us": ms * 1e3,
                          "algorithmic_flops_per_launch": flops,
                          "algorithmic_bytes_per_launch": nbytes,
@@ -399,7 +403,8 @@ def chain_leg(steps, warmup):
                 "hidden": "sign->repack u64", "epilogue": "alpha-scaled fp32",
                 "launch": "bnn_chain3 (fused)"},
         roofline={"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                  "frac": ach / HBM_PEAK_GBS,
+                  "traffic": recorded_traffic("chain_65536_traffic.md", CHAIN_SOURCES),
                   "kernel": "chain3_kernel (pack + 3 layers, one launch)",
                   "kernel_avg_us": ms_step * 1e3, "algorithmic_bytes_per_launch": nbytes,
                   "mfma_frac": ops / (ms_step * 1e-3) / MFMA_FP4_PEAK_OPS},
