@@ -87,7 +87,7 @@ __device__ __forceinline__ uint32_t x_at(const uint16_t *x, int64_t ldx, int64_t
 constexpr int kGemvRows = 8;          // activation rows per launch of the GEMV form
 constexpr int kUnitPadBytes = 16;     // LDS pad per unit (spreads lanes over banks)
 
-template <int L, int VEC, int P, bool SCALED>
+template <int L, int VEC, int P, bool SCALED, bool XV8>
 __global__ void __launch_bounds__(256)
     gemv_signw_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint64_t *__restrict__ wp,
                       const float *__restrict__ alpha, float *__restrict__ y, int M, int N, int K,
@@ -107,18 +107,36 @@ __global__ void __launch_bounds__(256)
   const uint32_t mask = kSignMask, ones = kPlusOnes;
 
   // Stage the activation rows once per block in pair order: word p of chunk
-  // q holds (x[32q + p], x[32q + p + 16]).
+  // q holds (x[32q + p], x[32q + p + 16]).  Item i builds words 4j .. 4j+3
+  // of one chunk (one 16-byte LDS store) from the 8-byte pieces
+  // x[32q + 4j .. +3] and x[32q + 16 + 4j .. +3]; pieces that reach past K
+  // (or rows that are not 8-byte aligned) are read element by element.
   {
     const int chunks = units * VEC * 2;
-    const int total = M * chunks * 16;
+    const int total = M * chunks * 4;
     for (int i = tid; i < total; i += 256) {
-      const int p = i & 15;
-      const int rq = i >> 4;
+      const int j = i & 3;
+      const int rq = i >> 2;
       const int m = rq / chunks, q = rq - m * chunks;
-      const int64_t k = (int64_t)q * 32 + p;
-      const uint32_t v = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 16, K) << 16);
+      const int64_t k = (int64_t)q * 32 + 4 * j;
+      uint32_t lo0, lo1, hi0, hi1;
+      if (XV8 && k + 20 <= K) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(x + m * ldx + k);
+        const uint2 b = *reinterpret_cast<const uint2 *>(x + m * ldx + k + 16);
+        lo0 = a.x; lo1 = a.y; hi0 = b.x; hi1 = b.y;
+      } else {
+        lo0 = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 1, K) << 16);
+        lo1 = x_at(x, ldx, m, k + 2, K) | (x_at(x, ldx, m, k + 3, K) << 16);
+        hi0 = x_at(x, ldx, m, k + 16, K) | (x_at(x, ldx, m, k + 17, K) << 16);
+        hi1 = x_at(x, ldx, m, k + 18, K) | (x_at(x, ldx, m, k + 19, K) << 16);
+      }
+      uint4 v;
+      v.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
+      v.y = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
+      v.z = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
+      v.w = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
       const int u = q / (VEC * 2), qi = q - u * (VEC * 2);
-      *reinterpret_cast<uint32_t *>(xs + ((size_t)m * units + u) * kUnitBytes + qi * 64 + p * 4) = v;
+      *reinterpret_cast<uint4 *>(xs + ((size_t)m * units + u) * kUnitBytes + qi * 64 + j * 16) = v;
     }
     __syncthreads();
   }
@@ -458,13 +476,19 @@ __global__ void __launch_bounds__(256, MINB)
 template <int L, int VEC, int P, bool SCALED>
 hipError_t launch_gemv_lp(const uint16_t *x, int64_t ldx, const uint64_t *wp, const float *alpha,
                           float *y, int M, int N, int K, int kw, hipStream_t s) {
+  // 8-byte activation pieces need 8-byte aligned row starts.
+  const bool xv8 = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0 || M == 1);
   constexpr int CB = 4 * (64 / L) * P;
   const int64_t steps = ((int64_t)N + CB - 1) / CB;
   const int64_t cap = 256 * 8;
   const int64_t blocks = steps < cap ? steps : cap;
   const size_t shmem = signw_gemv_lds_bytes(M, kw, VEC);
-  hipLaunchKernelGGL((gemv_signw_kernel<L, VEC, P, SCALED>), dim3((unsigned)blocks), dim3(256),
-                     shmem, s, x, ldx, wp, alpha, y, M, N, K, kw);
+  if (xv8)
+    hipLaunchKernelGGL((gemv_signw_kernel<L, VEC, P, SCALED, true>), dim3((unsigned)blocks),
+                       dim3(256), shmem, s, x, ldx, wp, alpha, y, M, N, K, kw);
+  else
+    hipLaunchKernelGGL((gemv_signw_kernel<L, VEC, P, SCALED, false>), dim3((unsigned)blocks),
+                       dim3(256), shmem, s, x, ldx, wp, alpha, y, M, N, K, kw);
   return hipGetLastError();
 }
 
