@@ -51,17 +51,22 @@ constexpr int kPipeTiles = BNN_CHAIN_PIPE;
 // into the 64-bit words of the wave's 32 rows: out[r * nw + wi].
 // acc[v]: row 8 (v / 4) + 4 h + v % 4, column li (+ 32 for the second tile);
 // the low ballot bits are row r's 32 columns, the high bits those of row r + 4.
+// The two ballots are wave-uniform, so both rows' words are put together
+// in scalar registers and lane 0 writes them (no per-lane select).
 __device__ __forceinline__ void repack_pair(const v16f &t0, const v16f &t1, uint64_t *out, int nw,
                                             int wi, int lane) {
-  const int h = lane >> 5, li = lane & 31;
+  uint64_t *col = out + wi;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const uint64_t lo = __builtin_amdgcn_ballot_w64(t0[v] <= 0.0f);
     const uint64_t hi = __builtin_amdgcn_ballot_w64(t1[v] <= 0.0f);
-    const int r = 8 * (v >> 2) + (v & 3) + 4 * h;  // lane 0: row r, lane 32: row r + 4
-    const uint64_t word = h ? ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32))
-                            : ((hi << 32) | (lo & 0xFFFFFFFFull));
-    if (li == 0) out[r * nw + wi] = word;
+    const int r = 8 * (v >> 2) + (v & 3);
+    const uint64_t w_r = (hi << 32) | (lo & 0xFFFFFFFFull);           // lanes 0-31: row r
+    const uint64_t w_r4 = (hi & 0xFFFFFFFF00000000ull) | (lo >> 32);  // lanes 32-63: row r + 4
+    if (lane == 0) {
+      col[r * nw] = w_r;
+      col[(r + 4) * nw] = w_r4;
+    }
   }
 }
 
@@ -151,15 +156,19 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   // slot q -> row q / 2, word (q % 2) hw0 + b; lane group g builds slots
   // 8j + g.  Lanes 0-31 of an MFMA take word b of their row, lanes 32-63
   // word hw0 + b, so batch b feeds exactly the layer-1 MFMAs of step b.
+  // Element offset of slot j's first element in step 0 (rows clamped into
+  // [0, M)); step b adds 64 b.
+  int64_t slot0[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = 8 * j + g;
+    int64_t m = row0 + (q >> 1);
+    m = m < M ? m : M - 1;
+    slot0[j] = m * ldx + (int64_t)((q & 1) * hw0) * 64 + 8 * t;
+  }
   auto load_batch = [&](int b, Raw8(&raw)[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int q = 8 * j + g;
-      int64_t m = row0 + (q >> 1);
-      m = m < M ? m : M - 1;
-      const int wd = (q & 1) * hw0 + b;
-      raw[j] = load_raw8<DT, VEC>(x, m * ldx + (int64_t)wd * 64 + 8 * t, 8);
-    }
+    for (int j = 0; j < 8; ++j) raw[j] = load_raw8<DT, VEC>(x, slot0[j] + 64 * b, 8);
   };
   auto pack_batch = [&](int b, const Raw8(&raw)[8]) {
 #pragma unroll
