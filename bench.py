@@ -273,6 +273,37 @@ def signw_gemv_leg(steps, warmup, ring=256, eager=False):
                          "algorithmic_bytes_per_launch": nbytes}}
 
 
+def signw_cpu_baseline(workload, seconds):
+    """The oracle's real-activation product (float64 sums) on a bounded
+    sample of the same workload: whole batch-1 steps, or a few rows of the
+    16384-row GEMM against every column."""
+    import numpy as np
+    import oracle
+    import workloads
+    d = workloads.make("gemv_4096" if workload == "signw_gemv_4096" else "signw_16384")
+    K = d["K"]
+    wp = oracle.pack(d["w"].numpy())
+    N = wp.shape[0]
+    rows = 1 if workload == "signw_gemv_4096" else 8
+    xb = workloads.bf16_bits(d["x"][:rows])
+    cores = os.cpu_count() or 1
+    n, t0 = 0, time.perf_counter()
+    while True:
+        s = oracle.dot_signw_bf16(xb, wp, K, nthreads=cores)
+        _ = s * d["alpha"].numpy().astype(np.float64)[None, :]
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    if rows == 1:
+        nbytes = N * oracle.words(K) * 8 + K * 2 + 8 * N
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} full batch-1 steps, {dt * 1e3:.1f} ms each (one row: one thread)"}
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s",
+            "cores": min(cores, rows), "kind": "oracle",
+            "sample": f"{n} x {rows} rows against all {N} columns, {dt:.2f} s each"}
+
+
 def signw_gemm_leg(steps, warmup):
     """Real bf16 activations (16384 x 1024) times packed sign weights
     (1024 x 1024), alpha-scaled fp32 output: the largest packed-kernel shape
@@ -386,11 +417,25 @@ def chain_leg(steps, warmup):
         # layer with the packed hidden rows kept on chip (bit-identical)
         bnn.chain3(x, wps[0], wps[1], wps[2], alpha, out=y)
 
+    # layer 1 with a folded BatchNorm (per-channel threshold + flip mask)
+    # against the plain sign -> repack of the same layer
+    g = workloads.generator(3003)
+    thr = (workloads.normal(g, dims[1]) * 8).round().to(torch.int32).to(dev)
+    flip = bnn.flip_words((workloads.normal(g, dims[1]) < 0).to(torch.int32).to(dev))
+
+    def layer1():
+        bnn.gemm_sign_repack(h0, wps[0], dims[0], out=h1)
+
+    def layer1_thr():
+        bnn.gemm_sign_repack_thr(h0, wps[0], thr, dims[0], flip, out=h1)
+
     for _ in range(max(warmup, 1)):
         step()
         fused()
     ms_sep = timed(step, steps, stream)
     ms_step = timed(fused, steps, stream)
+    ms_l1 = timed(layer1, steps, stream)
+    ms_l1_thr = timed(layer1_thr, steps, stream)
     ops = sum(2.0 * M * dims[i] * dims[i + 1] for i in range(3))
     # HBM bytes of the fused launch: the fp32 input, the fp32 output, the
     # packed weights and the scales
@@ -410,6 +455,9 @@ def chain_leg(steps, warmup):
                   "mfma_frac": ops / (ms_step * 1e-3) / MFMA_FP4_PEAK_OPS},
         unfused={"us_per_step": ms_sep * 1e3, "launches": 4,
                  "value": ops / (ms_sep * 1e-3) / 1e9},
+        threshold_repack={"layer": "512 -> 256 at M=65536 (gemm_mfma_kernel)",
+                          "plain_us": ms_l1 * 1e3, "threshold_flip_us": ms_l1_thr * 1e3,
+                          "binary_gops": 2.0 * M * dims[0] * dims[1] / (ms_l1_thr * 1e-3) / 1e9},
         step_inputs=(d, None, None),
     )
 
@@ -530,6 +578,8 @@ def main():
         out["ablation"] = res["ablation"]
     if "unfused" in res:
         out["unfused"] = res["unfused"]
+    if "threshold_repack" in res:
+        out["threshold_repack"] = res["threshold_repack"]
     if args.workload == "gemv_4096" and not args.no_secondary and not args.rows:
         sec = ffn_leg(10, 2)
         log(f"[bench] secondary ffn_4096: {sec['value']:.1f} binary GOPS")
@@ -542,8 +592,14 @@ def main():
         for leg in (signw_gemv_leg(1024, 64), signw_gemm_leg(20, 3)):
             log(f"[bench] {leg['workload']}: {leg['value']:.1f} {leg['unit']}, "
                 f"{leg['ms_per_step'] * 1e3:.2f} us/step")
-            out["signw"].append({k: leg[k] for k in ("workload", "value", "unit", "ms_per_step",
-                                                     "config", "roofline")})
+            rec = {k: leg[k] for k in ("workload", "value", "unit", "ms_per_step", "config",
+                                       "roofline")}
+            if not args.no_cpu_baseline:
+                rec["cpu_baseline"] = signw_cpu_baseline(leg["workload"], 3.0)
+            out["signw"].append(rec)
+    if not args.no_cpu_baseline and args.workload.startswith("signw"):
+        log("[bench] timing the CPU oracle ...")
+        out["cpu_baseline"] = signw_cpu_baseline(args.workload, args.cpu_seconds)
     if not args.no_cpu_baseline and res["step_inputs"] is not None:
         log("[bench] timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(args.workload, res["step_inputs"], args.cpu_seconds)

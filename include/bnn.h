@@ -238,7 +238,8 @@ bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, c
  * and packed; layer 1 (w1: N1 x bnn_words(K0)) and layer 2 (w2: N2 x
  * bnn_words(N1)) end in sign -> repack; layer 3 (w3: N3 x bnn_words(N2))
  * ends in fp32, times alpha3[n] when alpha3 is non-NULL.  The result is bit
- * for bit that of bnn_pack_signs, bnn_gemm_sign_repack (twice) and
+ * for bit that of bnn_pack_signs, bnn_gemm_sign_repack (twice; or
+ * bnn_gemm_sign_repack_thr with the thresholds below) and
  * bnn_gemm_u64_scaled (or the int32 dot as fp32 when alpha3 is NULL); the
  * packed hidden activations stay on chip.  ("Encoder / decoder",
  * BinaryAutoEncoder, and the balanced_ternary_engine README 512 -> 256 ->
@@ -248,6 +249,14 @@ bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, c
  *   x        M x ldx values of type dtype (BNN_FP32 / BNN_BF16), ldx >= K0,
  *            element-aligned.
  *   w1..w3   packed weights as above, 8-byte aligned.
+ *   thr1, flip1 / thr2, flip2
+ *            optional threshold repack of hidden layer 1 / 2, exactly as
+ *            bnn_gemm_sign_repack_thr: int32 thresholds per output channel
+ *            (N1 / N2 of them, 4-byte aligned) and packed flip masks
+ *            (bnn_words(N1) / bnn_words(N2) words, 8-byte aligned); either
+ *            may be NULL (threshold 0 / no flips), so all NULL is the plain
+ *            sign -> repack.  A BatchNorm after each hidden binary layer
+ *            folds into them ("Architecture Decision Record", Decision).
  *   alpha3   N3 fp32 scales, 4-byte aligned, or NULL.
  *   y        M x N3 fp32 output, row-major, 4-byte aligned.
  * Supported layer sizes: K0, N1, N2 in {128, 256, 384, 512}; N3 a multiple
@@ -256,8 +265,10 @@ bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, c
  * BNN_E_ALIGN, BNN_E_LAUNCH.
  */
 bnn_status bnn_chain3(const void *x, int dtype, int64_t ldx, const uint64_t *w1,
-                      const uint64_t *w2, const uint64_t *w3, const float *alpha3, float *y,
-                      int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3, void *stream);
+                      const int32_t *thr1, const uint64_t *flip1, const uint64_t *w2,
+                      const int32_t *thr2, const uint64_t *flip2, const uint64_t *w3,
+                      const float *alpha3, float *y, int64_t M, int64_t K0, int64_t N1, int64_t N2,
+                      int64_t N3, void *stream);
 
 /*
  * bnn_gemm_ex -- the general form of the three products above, with an

@@ -75,7 +75,7 @@ def library():
     lib.bnn_gemv_act.argtypes = [P, I, I64, P, P, P, I64, I64, I64, I, P]
     lib.bnn_gemm_sign_repack_thr.argtypes = [P, P, P, P, P, I64, I64, I64, I, P]
     lib.bnn_gemm_signw_bf16.argtypes = [P, I64, P, P, P, I64, I64, I64, I, P]
-    lib.bnn_chain3.argtypes = [P, I, I64, P, P, P, P, P, I64, I64, I64, I64, I64, P]
+    lib.bnn_chain3.argtypes = [P, I, I64, P, P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, P]
     for name in ("bnn_pack_signs", "bnn_gemm_u64", "bnn_gemm_u64_scaled", "bnn_gemm_sign_repack",
                  "bnn_gemm_ex", "bnn_gemv_act", "bnn_gemm_sign_repack_thr", "bnn_gemm_signw_bf16",
                  "bnn_chain3"):
@@ -295,13 +295,15 @@ def gemm_signw_bf16(x, wp, K=None, alpha=None, algo=ALGO_AUTO, out=None):
     return out
 
 
-def chain3(x, w1, w2, w3, alpha3=None, out=None):
+def chain3(x, w1, w2, w3, alpha3=None, out=None, thr1=None, flip1=None, thr2=None, flip2=None):
     """fp32 ``(M, N3)``: three chained binary layers in one launch
     (bnn_chain3).  ``x`` is a 2-D fp32 or bf16 CUDA tensor (unit stride along
     its last dimension, K0 columns); ``w1``, ``w2``, ``w3`` are packed weights
     ``(N1, words(K0))``, ``(N2, words(N1))``, ``(N3, words(N2))``; ``alpha3`` is
-    None or a contiguous float32 ``(N3,)``.  Equal, bit for bit, to pack_signs
-    -> gemm_sign_repack -> gemm_sign_repack -> gemm_u64_scaled."""
+    None or a contiguous float32 ``(N3,)``.  ``thr1``/``flip1`` and
+    ``thr2``/``flip2`` optionally make the hidden layers threshold repacks
+    (as gemm_sign_repack_thr).  Equal, bit for bit, to pack_signs ->
+    gemm_sign_repack(_thr) -> gemm_sign_repack(_thr) -> gemm_u64_scaled."""
     _need_cuda("x", x)
     if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
         raise ValueError("x must be 2-D with unit stride along its last dimension")
@@ -319,9 +321,20 @@ def chain3(x, w1, w2, w3, alpha3=None, out=None):
         _need_cuda("alpha3", alpha3)
         if alpha3.dtype != torch.float32 or alpha3.shape != (N3,) or not alpha3.is_contiguous():
             raise ValueError("alpha3 must be a contiguous float32 tensor of shape (N3,)")
+    for name, t, n in (("thr1", thr1, N1), ("thr2", thr2, N2)):
+        if t is not None:
+            _need_cuda(name, t)
+            if t.dtype != torch.int32 or tuple(t.shape) != (n,) or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 tensor of shape ({n},)")
+    for name, f, n in (("flip1", flip1, N1), ("flip2", flip2, N2)):
+        if f is not None:
+            _need_cuda(name, f)
+            if f.dtype != torch.int64 or tuple(f.shape) != (words(n),) or not f.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int64 tensor of shape ({words(n)},)")
     out = _out_for(EPI_SCALED, M, N3, x.device, out)
     ldx = x.stride(0) if M > 1 else max(K0, 1)
-    st = library().bnn_chain3(_ptr(x), dt, ldx, _ptr(w1), _ptr(w2), _ptr(w3), _ptr(alpha3),
-                              _ptr(out), M, K0, N1, N2, N3, _stream(x))
+    st = library().bnn_chain3(_ptr(x), dt, ldx, _ptr(w1), _ptr(thr1), _ptr(flip1), _ptr(w2),
+                              _ptr(thr2), _ptr(flip2), _ptr(w3), _ptr(alpha3), _ptr(out), M, K0, N1,
+                              N2, N3, _stream(x))
     _check(st, "bnn_chain3")
     return out

@@ -147,19 +147,23 @@ bnn_status bnn_gemm_signw_bf16(const void *x, int64_t ldx, const uint64_t *wp, c
 }
 
 bnn_status bnn_chain3(const void *x, int dtype, int64_t ldx, const uint64_t *w1,
-                      const uint64_t *w2, const uint64_t *w3, const float *alpha3, float *y,
-                      int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3, void *stream) {
+                      const int32_t *thr1, const uint64_t *flip1, const uint64_t *w2,
+                      const int32_t *thr2, const uint64_t *flip2, const uint64_t *w3,
+                      const float *alpha3, float *y, int64_t M, int64_t K0, int64_t N1, int64_t N2,
+                      int64_t N3, void *stream) {
   if (dtype != BNN_FP32 && dtype != BNN_BF16) return BNN_E_DTYPE;
   if (M < 0 || M >= kMaxDim || ldx < K0 || ldx >= kMaxDim ||
       !bnn::chain3_dims_ok(K0, N1, N2, N3))
     return BNN_E_SHAPE;
   if ((M > 0 && (!x || !y)) || !w1 || !w2 || !w3) return BNN_E_NULL;
   if (misaligned(x, dtype == BNN_FP32 ? 4 : 2) || misaligned(w1, 8) || misaligned(w2, 8) ||
-      misaligned(w3, 8) || misaligned(y, 4) || misaligned(alpha3, 4))
+      misaligned(w3, 8) || misaligned(y, 4) || misaligned(alpha3, 4) || misaligned(thr1, 4) ||
+      misaligned(thr2, 4) || misaligned(flip1, 8) || misaligned(flip2, 8))
     return BNN_E_ALIGN;
   if (M == 0) return BNN_OK;
+  const bnn::Chain3Repack rp{thr1, flip1, thr2, flip2};
   return launch_status(bnn::launch_chain3(x, dtype, ldx, w1, w2, w3, alpha3, y, M, K0, N1, N2, N3,
-                                          static_cast<hipStream_t>(stream)));
+                                          rp, static_cast<hipStream_t>(stream)));
 }
 
 bnn_status bnn_gemm_u64(const uint64_t *xp, const uint64_t *wp, int32_t *y, int64_t M, int64_t N,

@@ -69,10 +69,18 @@ hipError_t launch_signw_mfma(const uint16_t *x, int64_t ldx, const uint64_t *wp,
 // packed weights of all three layers and each wave's hidden rows live in
 // LDS, at most this many bytes.
 constexpr int64_t kChain3MaxLds = 64 * 1024;
+// Optional threshold repack of the two hidden layers (null: plain).
+struct Chain3Repack {
+  const int32_t *thr1;
+  const uint64_t *flip1;
+  const int32_t *thr2;
+  const uint64_t *flip2;
+};
 bool chain3_dims_ok(int64_t K0, int64_t N1, int64_t N2, int64_t N3);
 hipError_t launch_chain3(const void *x, int dtype, int64_t ldx, const uint64_t *w1,
                          const uint64_t *w2, const uint64_t *w3, const float *alpha, float *y,
-                         int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3, hipStream_t s);
+                         int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3,
+                         const Chain3Repack &rp, hipStream_t s);
 
 // Threshold-repack operands, loaded by the kernels before their K loops from
 // clamped (always in-bounds) indexes: the threshold of output column n, and

@@ -27,6 +27,9 @@
 //  * The repack epilogue ballots the signs of two neighbouring 32-column
 //    tiles into 64-bit words (as the GEMM does) and writes them to LDS as
 //    the next layer's rows; the last layer stores alpha-scaled fp32.
+//    Optional per-column thresholds and flip masks make each hidden layer's
+//    projection a folded BatchNorm ("Architecture Decision Record",
+//    Decision: BN after the binary layers), as bnn_gemm_sign_repack_thr.
 #include "../../include/bnn.h"
 #include "bnn_internal.h"
 #include "fp4_ops.h"
@@ -52,17 +55,24 @@ constexpr int kPipeTiles = BNN_CHAIN_PIPE;
 // acc[v]: row 8 (v / 4) + 4 h + v % 4, column li (+ 32 for the second tile);
 // the low ballot bits are row r's 32 columns, the high bits those of row r + 4.
 // The two ballots are wave-uniform, so both rows' words are put together
-// in scalar registers and lane 0 writes them (no per-lane select).
+// in scalar registers and lane 0 writes them (no per-lane select).  A bit is
+// set where the exact dot is <= the column's bound (tb: the layer's
+// per-column thresholds as exact fp32 bounds, 0 without thresholds), then
+// the group's flip word is applied.
+template <bool THR>
 __device__ __forceinline__ void repack_pair(const v16f &t0, const v16f &t1, uint64_t *out, int nw,
-                                            int wi, int lane) {
+                                            int wi, int lane, const float *tb, const uint64_t *fw) {
   uint64_t *col = out + wi;
+  const int li = lane & 31;
+  const float b0 = THR ? tb[64 * wi + li] : 0.0f, b1 = THR ? tb[64 * wi + 32 + li] : 0.0f;
+  const uint64_t f = THR ? fw[wi] : 0;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const uint64_t lo = __builtin_amdgcn_ballot_w64(t0[v] <= 0.0f);
-    const uint64_t hi = __builtin_amdgcn_ballot_w64(t1[v] <= 0.0f);
+    const uint64_t lo = __builtin_amdgcn_ballot_w64(t0[v] <= b0);
+    const uint64_t hi = __builtin_amdgcn_ballot_w64(t1[v] <= b1);
     const int r = 8 * (v >> 2) + (v & 3);
-    const uint64_t w_r = (hi << 32) | (lo & 0xFFFFFFFFull);           // lanes 0-31: row r
-    const uint64_t w_r4 = (hi & 0xFFFFFFFF00000000ull) | (lo >> 32);  // lanes 32-63: row r + 4
+    const uint64_t w_r = ((hi << 32) | (lo & 0xFFFFFFFFull)) ^ f;           // lanes 0-31: row r
+    const uint64_t w_r4 = ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32)) ^ f;  // lanes 32-63: row r + 4
     if (lane == 0) {
       col[r * nw] = w_r;
       col[(r + 4) * nw] = w_r4;
@@ -76,11 +86,11 @@ __device__ __forceinline__ void repack_pair(const v16f &t0, const v16f &t1, uint
 // fp32 outputs (times alpha[n] when alpha is non-null) go to rows row0.. of
 // y (those < M).  Lane l holds row / column l % 32 and, of each operand's
 // words, the half l / 32.
-template <bool REPACK>
+template <bool REPACK, bool THR>
 __device__ __forceinline__ void chain_layer(const uint64_t *a, int kw, const uint64_t *w, int N,
-                                            int n_begin, uint64_t *out,
-                                            const float *__restrict__ alpha, float *__restrict__ y,
-                                            int64_t row0, int M, int lane) {
+                                            int n_begin, uint64_t *out, const float *tb,
+                                            const uint64_t *fw, const float *__restrict__ alpha,
+                                            float *__restrict__ y, int64_t row0, int M, int lane) {
   const int h = lane >> 5, li = lane & 31;
   const int hw = kw >> 1;  // words per lane half (kw is even)
   const uint32_t c8 = 0x88888888u, c2 = 0x22222222u;
@@ -113,7 +123,7 @@ __device__ __forceinline__ void chain_layer(const uint64_t *a, int kw, const uin
       }
     }
     if (REPACK) {
-      repack_pair(acc[0], acc[TP - 1], out, N >> 6, n0 >> 6, lane);
+      repack_pair<THR>(acc[0], acc[TP - 1], out, N >> 6, n0 >> 6, lane, tb, fw);
     } else {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -124,20 +134,32 @@ __device__ __forceinline__ void chain_layer(const uint64_t *a, int kw, const uin
   }
 }
 
-// LDS words: the three packed weight matrices, then per wave its packed
-// rows of the input and of the two hidden layers.
+// LDS words: the three packed weight matrices, the two hidden layers'
+// repack bounds (fp32, two per word) and flip words, then per wave its
+// packed rows of the input and of the two hidden layers.
 __host__ __device__ inline int64_t chain3_lds_words(int64_t K0, int64_t N1, int64_t N2,
                                                     int64_t N3) {
   const int64_t kw0 = K0 >> 6, kw1 = N1 >> 6, kw2 = N2 >> 6;
-  return N1 * kw0 + N2 * kw1 + N3 * kw2 + 4 * kRows * (kw0 + kw1 + kw2);
+  return N1 * kw0 + N2 * kw1 + N3 * kw2 + (N1 + N2) / 2 + kw1 + kw2 +
+         4 * kRows * (kw0 + kw1 + kw2);
 }
 
-template <int DT, bool VEC>
+// Repack bound of a hidden column: the threshold as an fp32 value that is
+// exact against the exact (|d| <= K) accumulators, +-inf outside [-K, K];
+// 0 (the plain projection) without thresholds.
+__device__ __forceinline__ float repack_bound(const int32_t *thr, int n, int K) {
+  if (!thr) return 0.0f;
+  const int32_t t = thr[n];
+  return t >= K ? __builtin_inff() : (t < -K ? -__builtin_inff() : (float)t);
+}
+
+// THR: the hidden layers repack against thresholds / flip masks.
+template <int DT, bool VEC, bool THR>
 __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
     chain3_kernel(const void *__restrict__ x, int64_t ldx, const uint64_t *__restrict__ w1,
                   const uint64_t *__restrict__ w2, const uint64_t *__restrict__ w3,
                   const float *__restrict__ alpha, float *__restrict__ y, int M, int K0, int N1,
-                  int N2, int N3) {
+                  int N2, int N3, const Chain3Repack rp) {
   extern __shared__ __attribute__((aligned(16))) uint64_t lds[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,7 +169,9 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   const int hw0 = kw0 >> 1;
   const int nw1 = N1 * kw0, nw2 = N2 * kw1, nw3 = N3 * kw2;
   uint64_t *W1 = lds, *W2 = W1 + nw1, *W3 = W2 + nw2;
-  uint64_t *h0 = W3 + nw3 + wave * kRows * (kw0 + kw1 + kw2);
+  float *TB1 = reinterpret_cast<float *>(W3 + nw3), *TB2 = TB1 + N1;
+  uint64_t *FW1 = W3 + nw3 + (N1 + N2) / 2, *FW2 = FW1 + kw1;
+  uint64_t *h0 = FW2 + kw2 + wave * kRows * (kw0 + kw1 + kw2);
   uint64_t *h1 = h0 + kRows * kw0, *h2 = h1 + kRows * kw1;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * kRows;
   const uint32_t c8 = 0x88888888u, c2 = 0x22222222u;
@@ -198,6 +222,16 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
         if (i < total) lds[i] = v[u];
       }
     }
+    // repack bounds and flip words of the hidden layers
+    for (int i = tid; THR && i < N1 + N2; i += 256)
+      TB1[i] = i < N1 ? repack_bound(rp.thr1, i, K0) : repack_bound(rp.thr2, i - N1, N1);
+    for (int i = tid; THR && i < kw1 + kw2; i += 256) {
+      const uint64_t *f = i < kw1 ? rp.flip1 : rp.flip2;
+      const int wi = i < kw1 ? i : i - kw1, n = i < kw1 ? N1 : N2;
+      uint64_t fv = f ? f[wi] : 0;
+      if (f && wi == ((n + 63) >> 6) - 1 && (n & 63)) fv &= (uint64_t(1) << (n & 63)) - 1;
+      FW1[i] = fv;
+    }
   }
   __syncthreads();
 
@@ -229,29 +263,39 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   }
 #pragma unroll
   for (int cp = 0; cp < kPipeTiles / 2; ++cp)
-    if (2 * cp < np) repack_pair(acc[2 * cp], acc[2 * cp + 1], h1, kw1, cp, lane);
+    if (2 * cp < np)
+      repack_pair<THR>(acc[2 * cp], acc[2 * cp + 1], h1, kw1, cp, lane, TB1, FW1);
   if (nt1 > kPipeTiles)  // wider first layers: the remaining columns from the packed rows
-    chain_layer<true>(h0, kw0, W1, N1, 32 * kPipeTiles, h1, nullptr, nullptr, row0, M, lane);
+    chain_layer<true, THR>(h0, kw0, W1, N1, 32 * kPipeTiles, h1, TB1, FW1, nullptr, nullptr,
+                           row0, M, lane);
   __syncthreads();
-  chain_layer<true>(h1, kw1, W2, N2, 0, h2, nullptr, nullptr, row0, M, lane);
+  chain_layer<true, THR>(h1, kw1, W2, N2, 0, h2, TB2, FW2, nullptr, nullptr, row0, M, lane);
   __syncthreads();
-  chain_layer<false>(h2, kw2, W3, N3, 0, nullptr, alpha, y, row0, M, lane);
+  chain_layer<false, false>(h2, kw2, W3, N3, 0, nullptr, nullptr, nullptr, alpha, y, row0, M,
+                            lane);
 }
 
 template <int DT>
 hipError_t launch_dt(const void *x, int64_t ldx, const uint64_t *w1, const uint64_t *w2,
                      const uint64_t *w3, const float *alpha, float *y, int64_t M, int64_t K0,
-                     int64_t N1, int64_t N2, int64_t N3, hipStream_t s) {
+                     int64_t N1, int64_t N2, int64_t N3, const Chain3Repack &rp, hipStream_t s) {
   const int64_t esize = DT == 0 ? 4 : 2;
   const bool vec = ((uintptr_t)x % 16 == 0) && ((ldx * esize) % 16 == 0 || M == 1);
   const unsigned blocks = (unsigned)((M + 4 * kRows - 1) / (4 * kRows));
   const size_t shmem = (size_t)chain3_lds_words(K0, N1, N2, N3) * sizeof(uint64_t);
-  if (vec)
-    hipLaunchKernelGGL((chain3_kernel<DT, true>), dim3(blocks), dim3(256), shmem, s, x, ldx, w1,
-                       w2, w3, alpha, y, (int)M, (int)K0, (int)N1, (int)N2, (int)N3);
+  const bool thr = rp.thr1 || rp.flip1 || rp.thr2 || rp.flip2;
+#define BNN_CHAIN_LAUNCH(V, T)                                                                 \
+  hipLaunchKernelGGL((chain3_kernel<DT, V, T>), dim3(blocks), dim3(256), shmem, s, x, ldx, w1, \
+                     w2, w3, alpha, y, (int)M, (int)K0, (int)N1, (int)N2, (int)N3, rp)
+  if (vec && thr)
+    BNN_CHAIN_LAUNCH(true, true);
+  else if (vec)
+    BNN_CHAIN_LAUNCH(true, false);
+  else if (thr)
+    BNN_CHAIN_LAUNCH(false, true);
   else
-    hipLaunchKernelGGL((chain3_kernel<DT, false>), dim3(blocks), dim3(256), shmem, s, x, ldx, w1,
-                       w2, w3, alpha, y, (int)M, (int)K0, (int)N1, (int)N2, (int)N3);
+    BNN_CHAIN_LAUNCH(false, false);
+#undef BNN_CHAIN_LAUNCH
   return hipGetLastError();
 }
 
@@ -265,9 +309,10 @@ bool chain3_dims_ok(int64_t K0, int64_t N1, int64_t N2, int64_t N3) {
 
 hipError_t launch_chain3(const void *x, int dtype, int64_t ldx, const uint64_t *w1,
                          const uint64_t *w2, const uint64_t *w3, const float *alpha, float *y,
-                         int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3, hipStream_t s) {
-  return dtype == 0 ? launch_dt<0>(x, ldx, w1, w2, w3, alpha, y, M, K0, N1, N2, N3, s)
-                    : launch_dt<1>(x, ldx, w1, w2, w3, alpha, y, M, K0, N1, N2, N3, s);
+                         int64_t M, int64_t K0, int64_t N1, int64_t N2, int64_t N3,
+                         const Chain3Repack &rp, hipStream_t s) {
+  return dtype == 0 ? launch_dt<0>(x, ldx, w1, w2, w3, alpha, y, M, K0, N1, N2, N3, rp, s)
+                    : launch_dt<1>(x, ldx, w1, w2, w3, alpha, y, M, K0, N1, N2, N3, rp, s);
 }
 
 }  // namespace bnn

@@ -173,8 +173,10 @@ def test_signw_validation(lib):
 
 
 def test_chain3_validation(lib):
-    f = lib.bnn_chain3
-    # (x, dtype, ldx, w1, w2, w3, alpha3, y, M, K0, N1, N2, N3, stream)
+    # (x, dtype, ldx, w1, thr1, flip1, w2, thr2, flip2, w3, alpha3, y, M, K0, N1, N2, N3, stream)
+    def f(x, dt, ldx, w1, w2, w3, a3, y, M, *dims_stream, thr1=None, flip1=None):
+        return lib.bnn_chain3(x, dt, ldx, w1, thr1, flip1, w2, None, None, w3, a3, y, M,
+                              *dims_stream)
     ok_dims = (512, 256, 128, 64)
     assert f(FAKE, 7, 512, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None) == E_DTYPE
     for dims in [(500, 256, 128, 64), (640, 256, 128, 64), (512, 192, 128, 64),
@@ -190,3 +192,7 @@ def test_chain3_validation(lib):
     assert f(FAKE, 0, 512, FAKE, FAKE, FAKE_ODD, None, FAKE, 4, *ok_dims, None) == E_ALIGN
     assert f(FAKE, 0, 512, FAKE, FAKE, FAKE, P(0x1001), FAKE, 4, *ok_dims, None) == E_ALIGN
     assert f(None, 1, 512, FAKE, FAKE, FAKE, None, None, 0, *ok_dims, None) == OK     # M = 0
+    assert f(FAKE, 0, 512, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None,
+             thr1=P(0x1002)) == E_ALIGN
+    assert f(FAKE, 0, 512, FAKE, FAKE, FAKE, None, FAKE, 4, *ok_dims, None,
+             flip1=P(0x1004)) == E_ALIGN
