@@ -389,6 +389,26 @@ def ffn_leg(steps, warmup):
     )
 
 
+def thr_cpu_baseline(h0, w1, thr, flip, dims, rows=2048):
+    """The oracle's threshold repack of chain layer 1 on its first `rows`
+    packed input rows (the same operands the GPU leg times)."""
+    import numpy as np
+    import oracle
+    xp = h0[:rows].cpu().numpy().view(np.uint64)
+    wp = w1.cpu().numpy().view(np.uint64)
+    t = thr.cpu().numpy()
+    fl = np.unpackbits(flip.cpu().numpy().view(np.uint8), bitorder="little")[: dims[1]]
+    cores = os.cpu_count() or 1
+    n, t0 = 0, time.perf_counter()
+    while n < 3 or time.perf_counter() - t0 < 1.0:
+        oracle.sign_repack_thr(xp, wp, t, dims[0], fl, nthreads=cores)
+        n += 1
+    dt = (time.perf_counter() - t0) / n
+    return {"value": 2.0 * rows * dims[0] * dims[1] / dt / 1e9, "unit": "binary GOPS",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{n} x {rows} rows of layer 1, {dt * 1e3:.1f} ms each"}
+
+
 def chain_leg(steps, warmup):
     import torch
     import packed_xor_popcount_amd as bnn
@@ -457,7 +477,8 @@ def chain_leg(steps, warmup):
                  "value": ops / (ms_sep * 1e-3) / 1e9},
         threshold_repack={"layer": "512 -> 256 at M=65536 (gemm_mfma_kernel)",
                           "plain_us": ms_l1 * 1e3, "threshold_flip_us": ms_l1_thr * 1e3,
-                          "binary_gops": 2.0 * M * dims[0] * dims[1] / (ms_l1_thr * 1e-3) / 1e9},
+                          "binary_gops": 2.0 * M * dims[0] * dims[1] / (ms_l1_thr * 1e-3) / 1e9,
+                          "cpu_baseline": thr_cpu_baseline(h0, wps[0], thr, flip, dims)},
         step_inputs=(d, None, None),
     )
 
