@@ -273,9 +273,9 @@ __global__ void __launch_bounds__(256)
 // values (M <= 8, DT 0 = fp32, 1 = bf16, K a multiple of 64, rows 16-byte
 // aligned), and every lane holds at most one unit (VEC words) of each W row
 // it serves (units <= L), so a block step is
-// one straight-line round: issue the W loads, then the activation loads
-// (first step of the block only), then the scale; pack the activations into
-// LDS while the W words are in flight; popcounts; reduction; epilogue.  The
+// one straight-line round: issue the scale loads, the activation loads
+// (first step of the block only), then the W loads; pack the activations
+// into LDS while the W words are in flight; popcounts; reduction; epilogue.  The
 // same arithmetic and epilogues as gemv_kernel.
 template <int EPI, int L, int VEC, int P, int DT>
 __global__ void __launch_bounds__(256)
@@ -356,6 +356,10 @@ __global__ void __launch_bounds__(256)
       t_pre = thr_of(ep, nb + lane, N);
       f_pre = flip_of(ep, nb >> 6, N);
     }
+    // The first step's activation loads go out ahead of the W loads: the
+    // packing that must follow them then overlaps the W latency.
+    Raw8 raw[kS];
+    if (first) x_round(0, raw);
     uint64_t w[P][VEC];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -371,8 +375,6 @@ __global__ void __launch_bounds__(256)
       }
     }
     if (first) {  // uniform: pack the activations once per block
-      Raw8 raw[kS];
-      x_round(0, raw);
       x_store(0, raw);
       for (int q0 = 32 * kS; q0 < total; q0 += 32 * kS) {
         x_round(q0, raw);
