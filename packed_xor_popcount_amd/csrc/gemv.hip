@@ -43,6 +43,9 @@ constexpr int kChunkWords = 512;  // fused packer: K-chunk held in LDS per row
 #ifndef BNN_GEMV_SMALL_P
 #define BNN_GEMV_SMALL_P 1
 #endif
+#ifndef BNN_GEMV_LARGE_P
+#define BNN_GEMV_LARGE_P 4  // passes per block step when streaming large W
+#endif
 constexpr int kBlocksPerCU = BNN_GEMV_BLOCKS_PER_CU;  // persistent grid size (x 256 CUs)
 
 template <int EPI, int L, int VEC, int P, int XT>
@@ -332,35 +335,33 @@ __global__ void __launch_bounds__(256)
     }
   };
 
-  bool first = true;
-  for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
+  // Operands of one block step, loaded before they are used: the scales (or
+  // threshold and flip word) of the columns this lane stores and this lane's
+  // W unit of each pass.  W and the scales come from clamped, always
+  // in-bounds addresses, so the loads are unconditional.
+  struct StepRegs {
+    float a[P];
+    int32_t t;
+    uint64_t f;
+    uint64_t w[P][VEC];
+  };
+  auto load_step = [&](int step, StepRegs &r) {
     const int64_t nb = (int64_t)step * CB;
-    // Scales of the columns this lane will store (int32 / scaled epilogues
-    // store from the reducing lanes), issued first: their latency then
-    // overlaps the W and activation loads instead of following the pack.
-    float a_pre[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      a_pre[p] = 0.0f;
+      r.a[p] = 0.0f;
       if (EPI == BNN_EPI_SCALED) {
         int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
         n = n < N ? n : N - 1;
-        a_pre[p] = ep.alpha[n];
+        r.a[p] = ep.alpha[n];
       }
     }
-    // Threshold of column nb + lane and flip word of the step (repack is
-    // stored by wave 0, one column per lane).
-    int32_t t_pre = 0;
-    uint64_t f_pre = 0;
-    if (EPI == kEpiRepackThr) {
-      t_pre = thr_of(ep, nb + lane, N);
-      f_pre = flip_of(ep, nb >> 6, N);
+    r.t = 0;
+    r.f = 0;
+    if (EPI == kEpiRepackThr) {  // repack is stored by wave 0, one column per lane
+      r.t = thr_of(ep, nb + lane, N);
+      r.f = flip_of(ep, nb >> 6, N);
     }
-    // The first step's activation loads go out ahead of the W loads: the
-    // packing that must follow them then overlaps the W latency.
-    Raw8 raw[kS];
-    if (first) x_round(0, raw);
-    uint64_t w[P][VEC];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
@@ -368,39 +369,32 @@ __global__ void __launch_bounds__(256)
       const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
       if (VEC == 2) {
         const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(src);
-        w[p][0] = v.x;
-        w[p][VEC - 1] = v.y;
+        r.w[p][0] = v.x;
+        r.w[p][VEC - 1] = v.y;
       } else {
-        w[p][0] = src[0];
+        r.w[p][0] = src[0];
       }
     }
-    if (first) {  // uniform: pack the activations once per block
-      x_store(0, raw);
-      for (int q0 = 32 * kS; q0 < total; q0 += 32 * kS) {
-        x_round(q0, raw);
-        x_store(q0, raw);
-      }
-      __syncthreads();
-      first = false;
-    }
-
+  };
+  auto run_step = [&](int step, const StepRegs &r) {
+    const int64_t nb = (int64_t)step * CB;
     uint32_t acc[P][kMR];
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int r = 0; r < kMR; ++r) acc[p][r] = 0;
+      for (int rr = 0; rr < kMR; ++rr) acc[p][rr] = 0;
     if (u_ok) {  // K is a multiple of 64: no tail word to mask
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         const int word = u * VEC + v;
 #pragma unroll
-        for (int r = 0; r < kMR; ++r) {
-          if (r >= M) break;
-          const uint64_t x = xs[r * kw + word];
+        for (int rr = 0; rr < kMR; ++rr) {
+          if (rr >= M) break;
+          const uint64_t x = xs[rr * kw + word];
 #pragma unroll
           for (int p = 0; p < P; ++p) {
-            const uint64_t d = x ^ w[p][v];
-            acc[p][r] = popc_acc((uint32_t)(d >> 32), popc_acc((uint32_t)d, acc[p][r]));
+            const uint64_t d = x ^ r.w[p][v];
+            acc[p][rr] = popc_acc((uint32_t)(d >> 32), popc_acc((uint32_t)d, acc[p][rr]));
           }
         }
       }
@@ -408,9 +402,9 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int r = 0; r < kMR; ++r) {
-        if (r >= M) break;
-        acc[p][r] = group_sum<L>(acc[p][r]);
+      for (int rr = 0; rr < kMR; ++rr) {
+        if (rr >= M) break;
+        acc[p][rr] = group_sum<L>(acc[p][rr]);
       }
 
     if (is_repack(EPI)) {
@@ -419,18 +413,18 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
         for (int p = 0; p < P; ++p)
 #pragma unroll
-          for (int r = 0; r < kMR; ++r) {
-            if (r >= M) break;
-            res[r][(p * 4 + wave) * G + sub] = acc[p][r];
+          for (int rr = 0; rr < kMR; ++rr) {
+            if (rr >= M) break;
+            res[rr][(p * 4 + wave) * G + sub] = acc[p][rr];
           }
       }
       __syncthreads();
       if (wave == 0) {
         const int64_t n = nb + lane;
-        for (int r = 0; r < M; ++r) {
-          const int dot = (int)((uint32_t)K - 2u * res[r][lane]);
-          const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= t_pre) ^ f_pre;
-          if (lane == 0) static_cast<uint64_t *>(yv)[(int64_t)r * nw + (nb >> 6)] = word;
+        for (int rr = 0; rr < M; ++rr) {
+          const int dot = (int)((uint32_t)K - 2u * res[rr][lane]);
+          const uint64_t word = __builtin_amdgcn_ballot_w64(n < N && dot <= r.t) ^ r.f;
+          if (lane == 0) static_cast<uint64_t *>(yv)[(int64_t)rr * nw + (nb >> 6)] = word;
         }
       }
     } else if (part == 0) {
@@ -440,17 +434,42 @@ __global__ void __launch_bounds__(256)
         const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
         if (n >= N) continue;
 #pragma unroll
-        for (int r = 0; r < kMR; ++r) {
-          if (r >= M) break;
-          const int dot = (int)((uint32_t)K - 2u * acc[p][r]);
-          const int64_t o = (int64_t)r * N + n;
+        for (int rr = 0; rr < kMR; ++rr) {
+          if (rr >= M) break;
+          const int dot = (int)((uint32_t)K - 2u * acc[p][rr]);
+          const int64_t o = (int64_t)rr * N + n;
           if (EPI == BNN_EPI_I32)
             static_cast<int32_t *>(yv)[o] = dot;
           else
-            static_cast<float *>(yv)[o] = __fmul_rn((float)dot, a_pre[p]);
+            static_cast<float *>(yv)[o] = __fmul_rn((float)dot, r.a[p]);
         }
       }
     }
+  };
+
+  // First step: the activation loads go out ahead of the W loads, so the
+  // packing that must follow them overlaps the W latency.  Later steps run
+  // in pairs whose operands are loaded one step ahead (blocks with several
+  // steps stream W continuously); a pair's second half exists only when the
+  // block has that step, so single-step blocks load nothing extra.  The two
+  // register sets are never copied (a copy would wait for its load).
+  Raw8 raw[kS];
+  x_round(0, raw);
+  StepRegs ra;
+  load_step(blockIdx.x, ra);
+  x_store(0, raw);
+  for (int q0 = 32 * kS; q0 < total; q0 += 32 * kS) {
+    x_round(q0, raw);
+    x_store(q0, raw);
+  }
+  __syncthreads();
+  for (int step = blockIdx.x; step < nsteps; step += 2 * gridDim.x) {
+    const int sb = step + gridDim.x, sa = step + 2 * gridDim.x;
+    StepRegs rb;
+    if (sb < nsteps) load_step(sb, rb);  // uniform
+    run_step(step, ra);
+    if (sa < nsteps) load_step(sa, ra);
+    if (sb < nsteps) run_step(sb, rb);
   }
 }
 
@@ -499,7 +518,7 @@ hipError_t launch_l(const Args &a, hipStream_t s) {
     constexpr int CB1 = 4 * (64 / L);
     if ((int64_t)a.N <= (int64_t)CB1 * 256 * kBlocksPerCU)
       return launch_lp<EPI, L, VEC, XT, BNN_GEMV_SMALL_P>(a, s);
-    return launch_lp<EPI, L, VEC, XT, 4>(a, s);
+    return launch_lp<EPI, L, VEC, XT, BNN_GEMV_LARGE_P>(a, s);
   }
 }
 
