@@ -301,7 +301,7 @@ def signw_cpu_baseline(workload, seconds):
                 "sample": f"{n} full batch-1 steps, {dt * 1e3:.1f} ms each (one row: one thread)"}
     return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s",
             "cores": min(cores, rows), "kind": "oracle",
-            "sample": f"{n} x {rows} rows against all {N} columns, {dt:.2f} s each"}
+            "sample": f"{n} x {rows} rows against all {N} columns, {dt * 1e3:.1f} ms each"}
 
 
 def signw_gemm_leg(steps, warmup):

@@ -106,6 +106,122 @@ __global__ void __launch_bounds__(256)
   const int nsteps = (N + CB - 1) / CB;
   const uint32_t mask = kSignMask, ones = kPlusOnes;
 
+
+  // Operands of one block step (the scales of this lane's columns and its W
+  // words of each pass, for units u = part, part + L, ... < units), loaded
+  // before they are used from clamped, always in-bounds addresses.
+  struct StepRegs {
+    float a[P];
+    uint64_t w[P][VEC];
+  };
+  auto load_step = [&](int step, StepRegs &r) {
+    const int64_t nb = (int64_t)step * CB;
+    int uu = part < units ? part : units - 1;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+      n = n < N ? n : N - 1;
+      r.a[p] = SCALED ? alpha[n] : 1.0f;
+      const uint64_t *src = wp + n * kw + (int64_t)uu * VEC;
+      if (VEC == 2) {
+        const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+        r.w[p][0] = t.x;
+        r.w[p][VEC - 1] = t.y;
+      } else {
+        r.w[p][0] = src[0];
+      }
+    }
+  };
+  auto run_step = [&](int step, const StepRegs &r0) {
+    const int64_t nb = (int64_t)step * CB;
+    float acc[P][kGemvRows];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int rr = 0; rr < kGemvRows; ++rr) acc[p][rr] = 0.0f;
+    for (int u = part; u < units; u += L) {
+      uint64_t w[P][VEC];
+      if (u == part) {  // the unit whose words were loaded ahead
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) w[p][v] = r0.w[p][v];
+      } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+          n = n < N ? n : N - 1;
+          const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
+          if (VEC == 2) {
+            const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+            w[p][0] = t.x;
+            w[p][VEC - 1] = t.y;
+          } else {
+            w[p][0] = src[0];
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < VEC; ++v)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // chunk qi = 2v + h of this unit: 16 pair registers per column
+          uint32_t b[P][16];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const uint32_t c = (uint32_t)(w[p][v] >> (32 * h));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) b[p][j] = sign_pair(c << (15 - j), mask, ones);
+          }
+#pragma unroll
+          for (int rr = 0; rr < kGemvRows; ++rr) {
+            if (rr >= M) break;
+            const unsigned char *xr =
+                xs + ((size_t)rr * units + u) * kUnitBytes + (2 * v + h) * 64;
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+              const uint4 xv = *reinterpret_cast<const uint4 *>(xr + 16 * j4);
+#pragma unroll
+              for (int p = 0; p < P; ++p) {
+                float a = acc[p][rr];
+                a = dot2(xv.x, b[p][4 * j4 + 0], a);
+                a = dot2(xv.y, b[p][4 * j4 + 1], a);
+                a = dot2(xv.z, b[p][4 * j4 + 2], a);
+                a = dot2(xv.w, b[p][4 * j4 + 3], a);
+                acc[p][rr] = a;
+              }
+            }
+          }
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int rr = 0; rr < kGemvRows; ++rr) {
+        if (rr >= M) break;
+        acc[p][rr] = group_sum_f32<L>(acc[p][rr]);
+      }
+    if (part == 0) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
+        if (n >= N) continue;
+#pragma unroll
+        for (int rr = 0; rr < kGemvRows; ++rr) {
+          if (rr >= M) break;
+          y[(int64_t)rr * N + n] = SCALED ? __fmul_rn(acc[p][rr], r0.a[p]) : acc[p][rr];
+        }
+      }
+    }
+  };
+
+  // The first step's W words and scales go out before the activation rows
+  // are staged, so the staging overlaps their latency; later steps run in
+  // pairs whose operands are loaded one step ahead (single-step blocks load
+  // nothing extra; the register sets are never copied).
+  StepRegs ra;
+  load_step(blockIdx.x, ra);
   // Stage the activation rows once per block in pair order: word p of chunk
   // q holds (x[32q + p], x[32q + p + 16]).  Item i builds words 4j .. 4j+3
   // of one chunk (one 16-byte LDS store) from the 8-byte pieces
@@ -140,90 +256,13 @@ __global__ void __launch_bounds__(256)
     }
     __syncthreads();
   }
-
-  for (int step = blockIdx.x; step < nsteps; step += gridDim.x) {
-    const int64_t nb = (int64_t)step * CB;
-    float a_pre[P];
-    const uint64_t *wrow[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
-      n = n < N ? n : N - 1;
-      wrow[p] = wp + n * kw;
-      a_pre[p] = SCALED ? alpha[n] : 1.0f;
-    }
-    float acc[P][kGemvRows];
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) acc[p][r] = 0.0f;
-
-    for (int u = part; u < units; u += L) {
-      uint64_t w[P][VEC];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint64_t *src = wrow[p] + (int64_t)u * VEC;
-        if (VEC == 2) {
-          const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
-          w[p][0] = t.x;
-          w[p][VEC - 1] = t.y;
-        } else {
-          w[p][0] = src[0];
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // chunk qi = 2v + h of this unit: 16 pair registers per column
-          uint32_t b[P][16];
-#pragma unroll
-          for (int p = 0; p < P; ++p) {
-            const uint32_t c = (uint32_t)(w[p][v] >> (32 * h));
-#pragma unroll
-            for (int j = 0; j < 16; ++j) b[p][j] = sign_pair(c << (15 - j), mask, ones);
-          }
-#pragma unroll
-          for (int r = 0; r < kGemvRows; ++r) {
-            if (r >= M) break;
-            const unsigned char *xr =
-                xs + ((size_t)r * units + u) * kUnitBytes + (2 * v + h) * 64;
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-              const uint4 xv = *reinterpret_cast<const uint4 *>(xr + 16 * j4);
-#pragma unroll
-              for (int p = 0; p < P; ++p) {
-                float a = acc[p][r];
-                a = dot2(xv.x, b[p][4 * j4 + 0], a);
-                a = dot2(xv.y, b[p][4 * j4 + 1], a);
-                a = dot2(xv.z, b[p][4 * j4 + 2], a);
-                a = dot2(xv.w, b[p][4 * j4 + 3], a);
-                acc[p][r] = a;
-              }
-            }
-          }
-        }
-    }
-
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
-        if (r >= M) break;
-        acc[p][r] = group_sum_f32<L>(acc[p][r]);
-      }
-    if (part == 0) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const int64_t n = nb + (int64_t)(p * 4 + wave) * G + sub;
-        if (n >= N) continue;
-#pragma unroll
-        for (int r = 0; r < kGemvRows; ++r) {
-          if (r >= M) break;
-          y[(int64_t)r * N + n] = SCALED ? __fmul_rn(acc[p][r], a_pre[p]) : acc[p][r];
-        }
-      }
-    }
+  for (int step = blockIdx.x; step < nsteps; step += 2 * gridDim.x) {
+    const int sb = step + gridDim.x, sa = step + 2 * gridDim.x;
+    StepRegs rb;
+    if (sb < nsteps) load_step(sb, rb);  // uniform
+    run_step(step, ra);
+    if (sa < nsteps) load_step(sa, ra);
+    if (sb < nsteps) run_step(sb, rb);
   }
 }
 
