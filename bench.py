@@ -226,7 +226,7 @@ def gemv_leg(args, steps, warmup):
                   "frac": achieved / HBM_PEAK_GBS,
                   "traffic": recorded_traffic("gemv_4096_traffic.md", GEMV_SOURCES)
                   if not args.rows else None,
-                  "kernel": "gemv_kernel (bf16 activations packed in-kernel, alpha-scaled)",
+                  "kernel": "gemv_act_kernel (bf16 activations packed in-kernel, alpha-scaled)",
                   "kernel_avg_us": ms_gemv * 1e3,
                   "algorithmic_bytes_per_launch": bytes_gemv},
         step_inputs=(d, N, K),
