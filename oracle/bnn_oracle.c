@@ -1,7 +1,7 @@
 /*
  * bnn_oracle.c -- plain, slow CPU oracle for packed binary (+1/-1) products.
  *
- * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * TEST INFRASTRUCTURE ONLY.  This file is the test oracle, not the product: only
  * the test-suite, the smoke check and the CPU-baseline leg of the benchmark
  * load it.  It shares no code, header, table or constant with the HIP library
  * and includes nothing from it.

@@ -15,8 +15,8 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests must never silently pass without a GPU: skip them loudly
-    # when no device is visible (the driver selects them with -m gpu on a
-    # GPU machine, where torch.cuda.is_available() is True).
+    # when no device is visible (select them with -m gpu on a machine with
+    # an MI355X, where torch.cuda.is_available() is True).
     try:
         import torch
         have_gpu = torch.cuda.is_available()
