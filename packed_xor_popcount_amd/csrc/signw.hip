@@ -35,6 +35,8 @@
 #include "../../include/bnn.h"
 #include "bnn_internal.h"
 
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
 namespace bnn {
 namespace {
 
@@ -123,12 +125,14 @@ __global__ void __launch_bounds__(256)
       n = n < N ? n : N - 1;
       r.a[p] = SCALED ? alpha[n] : 1.0f;
       const uint64_t *src = wp + n * kw + (int64_t)uu * VEC;
+      // W is read once per call: non-temporal loads keep it from
+      // displacing the staged activations' sources and the scales.
       if (VEC == 2) {
-        const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+        const u64x2 t = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(src));
         r.w[p][0] = t.x;
         r.w[p][VEC - 1] = t.y;
       } else {
-        r.w[p][0] = src[0];
+        r.w[p][0] = __builtin_nontemporal_load(src);
       }
     }
   };
@@ -153,11 +157,11 @@ __global__ void __launch_bounds__(256)
           n = n < N ? n : N - 1;
           const uint64_t *src = wp + n * kw + (int64_t)u * VEC;
           if (VEC == 2) {
-            const ulonglong2 t = *reinterpret_cast<const ulonglong2 *>(src);
+            const u64x2 t = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(src));
             w[p][0] = t.x;
             w[p][VEC - 1] = t.y;
           } else {
-            w[p][0] = src[0];
+            w[p][0] = __builtin_nontemporal_load(src);
           }
         }
       }
