@@ -217,19 +217,41 @@ def gemv_act(x: torch.Tensor, wp: torch.Tensor, K: int | None = None, epilogue: 
     return out
 
 
+def _named(name: str, xp, wp, K, epilogue: int, alpha, out):
+    """Marshal one of the three named products (same checks as gemm_ex) and
+    call its own C entry point."""
+    M = _packed("xp", xp, K)
+    N = _packed("wp", wp, K)
+    if wp.device != xp.device:
+        raise ValueError("xp and wp must be on the same device")
+    if epilogue == EPI_SCALED:
+        _need_cuda("alpha", alpha)
+        if alpha.dtype != torch.float32 or alpha.shape != (N,) or not alpha.is_contiguous():
+            raise ValueError("alpha must be a contiguous float32 tensor of shape (N,)")
+    out = _out_for(epilogue, M, N, xp.device, out)
+    fn = getattr(library(), name)
+    if epilogue == EPI_SCALED:
+        st = fn(_ptr(xp), _ptr(wp), _ptr(alpha), _ptr(out), M, N, int(K), _stream(xp))
+    else:
+        st = fn(_ptr(xp), _ptr(wp), _ptr(out), M, N, int(K), _stream(xp))
+    _check(st, name)
+    return out
+
+
 def gemm_u64(xp, wp, K, out=None):
-    """int32 ``(M, N)``: ``<x_m, w_n> = K - 2 * popcount(x_m XOR w_n)``."""
-    return gemm_ex(xp, wp, K, EPI_I32, ALGO_AUTO, None, out)
+    """int32 ``(M, N)``: ``<x_m, w_n> = K - 2 * popcount(x_m XOR w_n)`` (bnn_gemm_u64)."""
+    return _named("bnn_gemm_u64", xp, wp, K, EPI_I32, None, out)
 
 
 def gemm_u64_scaled(xp, wp, alpha, K, out=None):
-    """fp32 ``(M, N)``: ``(float)<x_m, w_n> * alpha[n]``."""
-    return gemm_ex(xp, wp, K, EPI_SCALED, ALGO_AUTO, alpha, out)
+    """fp32 ``(M, N)``: ``(float)<x_m, w_n> * alpha[n]`` (bnn_gemm_u64_scaled)."""
+    return _named("bnn_gemm_u64_scaled", xp, wp, K, EPI_SCALED, alpha, out)
 
 
 def gemm_sign_repack(xp, wp, K, out=None):
-    """int64 ``(M, words(N))``: projected signs of ``<x_m, w_n>`` packed along N."""
-    return gemm_ex(xp, wp, K, EPI_REPACK, ALGO_AUTO, None, out)
+    """int64 ``(M, words(N))``: projected signs of ``<x_m, w_n>`` packed along N
+    (bnn_gemm_sign_repack)."""
+    return _named("bnn_gemm_sign_repack", xp, wp, K, EPI_REPACK, None, out)
 
 
 def gemm_sign_repack_thr(xp, wp, thr, K, flip=None, algo=ALGO_AUTO, out=None):

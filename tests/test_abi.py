@@ -21,8 +21,8 @@ FAKE = P(0x1000)        # aligned, never dereferenced: every call below fails va
 FAKE_ODD = P(0x1003)    # misaligned
 
 
-def declared_symbols():
-    text = open(HEADER).read()
+def declared_symbols(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bnn_\w+)\s*\(", text)))
 
@@ -46,6 +46,30 @@ def test_library_exports_every_declared_symbol(lib):
     for s in declared_symbols():
         assert s in exported, s
         assert hasattr(lib, s)
+
+
+def test_calibration_library_exports_its_header():
+    """libbnn_calib.so (the benchmark's rate probes) loads and exports every
+    entry point include/bnn_calib.h declares; libbnn.so does not need it."""
+    from packed_xor_popcount_amd import calib
+    header = os.path.join(ROOT, "include", "bnn_calib.h")
+    syms = declared_symbols(header)
+    assert set(syms) == set(calib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", calib.library_path],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)", out))
+    lib = calib.library()
+    for s in syms:
+        assert s in exported, s
+        assert hasattr(lib, s)
+    # host-side validation, no launch
+    assert lib.bnn_calib_valu(None, 1, 1, None) == E_NULL
+    assert lib.bnn_calib_mfma_fp4(FAKE, 0, 1, None) == E_SHAPE
+    assert lib.bnn_calib_read(FAKE, 15, FAKE, 1, None) == E_SHAPE
+    assert lib.bnn_calib_read(FAKE_ODD, 16, FAKE, 1, None) == E_ALIGN
+    deps = subprocess.run(["readelf", "-d", bnn.library_path], capture_output=True, text=True,
+                          check=True).stdout
+    assert "bnn_calib" not in deps
 
 
 def test_library_is_gfx950_code():

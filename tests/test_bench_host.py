@@ -52,3 +52,44 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and not r.stdout.strip()
+
+
+@pytest.mark.parametrize("R", [2, 3, 17, 384])
+@pytest.mark.parametrize("steps", [1, 2, 5, 20, 383, 384, 385, 1024])
+@pytest.mark.parametrize("warmup", [0, 1, 5, 64])
+def test_ring_plan_keeps_timed_weights_cold(R, steps, warmup):
+    plan = bench.ring_plan(R, steps, warmup)
+    phases = [p for p, _ in plan]
+    assert phases[-1] == "timed" and phases[0] == "warm"
+    timed = plan[-1][1]
+    assert timed == [i % R for i in range(steps)]          # step i reads entry i mod R
+    warm = dict(plan)["warm"]
+    assert len(warm) == warmup
+    if steps + warmup <= R:
+        # eager warm-up never reads an entry the timed replay reads
+        assert not set(warm) & set(timed)
+    # between a timed read and the previous read of the same entry, every
+    # other ring entry is read once: R - 1 entries
+    assert bench.cold_gap_entries(plan) == R - 1
+
+
+def test_headline_ring_exceeds_the_infinity_cache():
+    # the driver's --steps 20 --warmup 5: each timed 2 MiB weight copy was
+    # last read before 383 other copies (766 MiB > 2 x 256 MB) were read
+    plan = bench.ring_plan(bench.GEMV_RING, 20, 5)
+    gap_bytes = bench.cold_gap_entries(plan) * 4096 * 64 * 8
+    assert gap_bytes >= 2 * bench.MALL_BYTES
+    assert "evict" in dict(plan)
+
+
+def test_cold_gap_detects_a_warm_replay():
+    # the protocol of the previous bench (no eviction pass between the graph
+    # warm-up replay and the timed replay) re-read the timed entries after
+    # steps - 1 others only; the checker must see that
+    plan = [("warm", [0, 1, 2]), ("graph", list(range(20))), ("timed", list(range(20)))]
+    assert bench.cold_gap_entries(plan) == 19
+
+
+def test_bench_parses_driver_flags():
+    a = bench.parse(["--gpus", "1", "--steps", "20", "--warmup", "5"])
+    assert (a.gpus, a.steps, a.warmup, a.workload) == (1, 20, 5, "gemv_4096")

@@ -347,6 +347,28 @@ def test_threads_do_not_change_results():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("k", [0, 1, 63, 64, 65, 1000, 4096])
+def test_unpack_round_trip_ignores_pad_bits(k):
+    """oracle.unpack against numpy's own bit unpacking ("Binary Math
+    Effectiveness", section 1 encoding table: bit 0 is +1, bit 1 is -1; pad
+    bits past the logical n are not elements), with garbage pad bits."""
+    rng = np.random.default_rng(100 + k)
+    p = rand_packed(rng, 9, k)
+    got = oracle.unpack(p | garbage_pads(rng, 9, k), k)
+    assert got.dtype == np.int8 and got.shape == (9, k)
+    assert np.array_equal(got.astype(np.int64), np_unpack(p, k))
+    # pack(unpack) is the identity on pad-free words
+    if k:
+        assert np.array_equal(oracle.pack(got.astype(np.float32), k), p)
+
+
+def test_unpack_worked_example():
+    """Word 0b...1101 with K = 4: elements 0, 2, 3 are -1 and element 1 is +1
+    (bit k of word 0 is element k, least significant bit first)."""
+    p = np.array([[0b1101 | (0xF0 << 56)]], dtype=np.uint64)
+    assert oracle.unpack(p, 4).tolist() == [[-1, 1, -1, -1]]
+
+
 # --------------------------------------------------------------------------
 # Mutation check: each plausible mistake planted in a copy of the oracle (on
 # the CPU) must fail at least one pin.
