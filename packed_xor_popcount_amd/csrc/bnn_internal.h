@@ -96,6 +96,14 @@ __device__ __forceinline__ uint64_t flip_of(const EpiParams &ep, int64_t wi, int
 }
 
 constexpr int kWave = 64;  // CDNA wavefront width
+
+// s_waitcnt operand: wait until no vector memory operation is outstanding
+// (the other counters unconstrained).  Kernels issue it once before an
+// epilogue of many stores whose values depend on earlier loads: with
+// nothing outstanding the stores need no waits, whereas the compiler,
+// losing track of such loads across the stores' branches, would otherwise
+// wait for every earlier store before each new one.
+constexpr int kWaitVmem0 = 0x0F70;
 constexpr int64_t kMfmaMaxK = int64_t(1) << 24;  // fp32 accumulation of +-1 is exact up to here
 
 // acc + popcount(v) as the single accumulate form of v_bcnt_u32_b32.  Written

@@ -86,10 +86,14 @@ __device__ __forceinline__ void repack_pair(const v16f &t0, const v16f &t1, uint
 // fp32 outputs (times alpha[n] when alpha is non-null) go to rows row0.. of
 // y (those < M).  Lane l holds row / column l % 32 and, of each operand's
 // words, the half l / 32.
+// alpha (fp32 outputs) is the scales' copy in LDS, or null for no scale:
+// reading it from LDS keeps the stores below free of waits on vector
+// memory (a scale register loaded from global memory makes the compiler
+// drain every earlier store before each new one).
 template <bool REPACK, bool THR>
 __device__ __forceinline__ void chain_layer(const uint64_t *a, int kw, const uint64_t *w, int N,
                                             int n_begin, uint64_t *out, const float *tb,
-                                            const uint64_t *fw, const float *__restrict__ alpha,
+                                            const uint64_t *fw, const float *alpha,
                                             float *__restrict__ y, int64_t row0, int M, int lane) {
   const int h = lane >> 5, li = lane & 31;
   const int hw = kw >> 1;  // words per lane half (kw is even)
@@ -125,22 +129,32 @@ __device__ __forceinline__ void chain_layer(const uint64_t *a, int kw, const uin
     if (REPACK) {
       repack_pair<THR>(acc[0], acc[TP - 1], out, N >> 6, n0 >> 6, lane, tb, fw);
     } else {
+      // rows row0 + 8 (v / 4) + v % 4 + 4h; a wave whose 32 rows all exist
+      // stores without a row test (straight-line stores)
+      float *yp = y + (row0 + 4 * h) * N + n0 + li;
+      auto put = [&](int v) __attribute__((always_inline)) {
+        yp[(int64_t)(8 * (v >> 2) + (v & 3)) * N] = alpha ? __fmul_rn(acc[0][v], a_n) : acc[0][v];
+      };
+      if (row0 + kRows <= M) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t r = row0 + 8 * (v >> 2) + (v & 3) + 4 * h;
-        if (r < M) y[r * N + n0 + li] = alpha ? __fmul_rn(acc[0][v], a_n) : acc[0][v];
+        for (int v = 0; v < 16; ++v) put(v);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (row0 + 8 * (v >> 2) + (v & 3) + 4 * h < M) put(v);
       }
     }
   }
 }
 
 // LDS words: the three packed weight matrices, the two hidden layers'
-// repack bounds (fp32, two per word) and flip words, then per wave its
-// packed rows of the input and of the two hidden layers.
+// repack bounds (fp32, two per word) and flip words, the last layer's
+// scales (fp32, two per word), then per wave its packed rows of the input
+// and of the two hidden layers.
 __host__ __device__ inline int64_t chain3_lds_words(int64_t K0, int64_t N1, int64_t N2,
                                                     int64_t N3) {
   const int64_t kw0 = K0 >> 6, kw1 = N1 >> 6, kw2 = N2 >> 6;
-  return N1 * kw0 + N2 * kw1 + N3 * kw2 + (N1 + N2) / 2 + kw1 + kw2 +
+  return N1 * kw0 + N2 * kw1 + N3 * kw2 + (N1 + N2) / 2 + kw1 + kw2 + N3 / 2 +
          4 * kRows * (kw0 + kw1 + kw2);
 }
 
@@ -171,7 +185,8 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   uint64_t *W1 = lds, *W2 = W1 + nw1, *W3 = W2 + nw2;
   float *TB1 = reinterpret_cast<float *>(W3 + nw3), *TB2 = TB1 + N1;
   uint64_t *FW1 = W3 + nw3 + (N1 + N2) / 2, *FW2 = FW1 + kw1;
-  uint64_t *h0 = FW2 + kw2 + wave * kRows * (kw0 + kw1 + kw2);
+  float *AL = reinterpret_cast<float *>(FW2 + kw2);
+  uint64_t *h0 = FW2 + kw2 + N3 / 2 + wave * kRows * (kw0 + kw1 + kw2);
   uint64_t *h1 = h0 + kRows * kw0, *h2 = h1 + kRows * kw1;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * kRows;
   const uint32_t c8 = 0x88888888u, c2 = 0x22222222u;
@@ -222,6 +237,8 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
         if (i < total) lds[i] = v[u];
       }
     }
+    // the last layer's scales
+    for (int i = tid; alpha && i < N3; i += 256) AL[i] = alpha[i];
     // repack bounds and flip words of the hidden layers
     for (int i = tid; THR && i < N1 + N2; i += 256)
       TB1[i] = i < N1 ? repack_bound(rp.thr1, i, K0) : repack_bound(rp.thr2, i - N1, N1);
@@ -271,8 +288,8 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   __syncthreads();
   chain_layer<true, THR>(h1, kw1, W2, N2, 0, h2, TB2, FW2, nullptr, nullptr, row0, M, lane);
   __syncthreads();
-  chain_layer<false, false>(h2, kw2, W3, N3, 0, nullptr, nullptr, nullptr, alpha, y, row0, M,
-                            lane);
+  chain_layer<false, false>(h2, kw2, W3, N3, 0, nullptr, nullptr, nullptr, alpha ? AL : nullptr,
+                            y, row0, M, lane);
 }
 
 template <int DT>

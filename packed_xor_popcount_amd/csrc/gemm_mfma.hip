@@ -25,12 +25,28 @@
 //  * pad elements (k >= K) get zero nibbles in the A operand, so they add
 //    nothing whatever the pad bits of either operand hold.
 //
-// Tiling: block = 4 waves arranged WR x WC; a wave owns RB x CB tiles of
-// 32 x 32 outputs.  Per step of 8 words (512 elements of K) each lane loads
-// its rows' / columns' words straight from L2 (lanes 0-31: words k0..k0+3;
-// lanes 32-63: words k0+4..k0+7; the eight MFMA slices pair the low or high
-// halves of those words), unpacks them in registers and issues RB*CB*8
-// MFMAs; the next step's words are loaded before the current step's MFMAs.
+// Work split.  A block is 4 waves arranged WR x WC; a wave owns RB x CB
+// tiles of 32 x 32 outputs.  The unpack costs 7 VALU ops per operand
+// register set and one set feeds CB (A) or RB (B) MFMAs of 32 cycles, so
+// VALU per MFMA = 7 (RB + CB) / (RB CB): 3.5 at 4 x 4 tiles, where the
+// matrix cores (not the VALU) set the pace.  The large configuration is
+// therefore 2 x 2 waves of 4 x 4 tiles (block tile 256 x 256, one wave per
+// SIMD, accumulators in the AGPRs); small shapes use 4 x 1 waves of 2 x 2.
+//
+// K loop.  A step is 8 words (512 elements of K): lanes 0-31 hold words
+// 8s .. 8s+3 of their row / column, lanes 32-63 words 8s+4 .. 8s+7; slice
+// (i, q) pairs half q of word i of both lane halves.  The words are read
+// with buffer loads through per-block resources: each lane's row offset is
+// fixed and the step offset is a scalar, so a step costs no vector address
+// arithmetic, and every load outside the block's rows returns 0 (no load
+// can leave the matrices).  Two register sets ping-pong: step s+1 is in
+// flight while step s runs.  Inside a step, slice j+1 is unpacked while
+// slice j's MFMAs run.
+//
+// Tile order.  Hardware places block b on XCD b % 8; block b takes logical
+// tile (b % 8) * (T / 8) + b / 8 (T tiles, column-tile major), so each
+// XCD's L2 holds all of X but only an eighth of W.
+//
 // Output layout of a 32 x 32 tile (lane l, accumulator register v): column
 // l % 32, row 8 (v / 4) + 4 (l / 32) + v % 4.  The repack epilogue ballots
 // two neighbouring tiles: the low 32 ballot bits are one row's 32 columns,
@@ -42,55 +58,99 @@
 namespace bnn {
 namespace {
 
-// Wave arrangement and per-wave tiles of the wide-output configuration.
-#ifndef BNN_MFMA_SW
-#define BNN_MFMA_SW 8  // words of K per register step
-#endif
-#ifndef BNN_MFMA_PIN
-#define BNN_MFMA_PIN 1  // pin each step's prefetch ahead of the step's MFMAs
-#endif
-#ifndef BNN_MFMA_SCHED
-#define BNN_MFMA_SCHED 0  // VALU ops to interleave after each MFMA (0: compiler's choice)
-#endif
-#ifndef BNN_MFMA_WR
-#define BNN_MFMA_WR 4
-#define BNN_MFMA_WC 1
-#define BNN_MFMA_RB 2
-#define BNN_MFMA_CB 2
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Large-product configuration (waves WR x WC, wave tiles RB x CB, words of
+// K per step, blocks per CU the register allocation must allow).
+#ifndef BNN_MFMA_BIG
+#define BNN_MFMA_BIG 2, 2, 4, 4, 4, 1
 #endif
 
+typedef int v4i __attribute__((ext_vector_type(4)));
 
-template <int EPI, int WR, int WC, int RB, int CB>
-__global__ void __launch_bounds__(256)
+// Operand registers (the four used nibble registers of an FP4 operand) of
+// the 32-bit chunk c: register r = ((c << (3 - r)) & 0x88888888) | 0x22222222.
+__device__ __forceinline__ v4i fp4_chunk(uint32_t c, uint32_t c8, uint32_t c2) {
+  v4i o;
+  o[0] = (int)and_or(c << 3, c8, c2);
+  o[1] = (int)and_or(c << 2, c8, c2);
+  o[2] = (int)and_or(c << 1, c8, c2);
+  o[3] = (int)and_or(c, c8, c2);
+  return o;
+}
+
+// The eight-register operand of the FP4 MFMA: an FP4 operand uses the first
+// four registers only.
+__device__ __forceinline__ v8i fp4_operand(v4i o) {
+  const v4i z = {0, 0, 0, 0};
+  return __builtin_shufflevector(o, z, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// mask_operand on the four used registers.
+__device__ __forceinline__ v4i mask4(v4i a, uint32_t valid) {
+  const v8i m = mask_operand(fp4_operand(a), valid);
+  return (v4i){m[0], m[1], m[2], m[3]};
+}
+
+// Scheduling groups of one slice: NM MFMAs, each followed by its share of NV
+// VALU ops (the shares differ by at most one).
+template <int I, int NM, int NV>
+__device__ __forceinline__ void interleave_groups() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, (NV * (I + 1)) / NM - (NV * I) / NM, 0);
+    interleave_groups<I + 1, NM, NV>();
+  }
+}
+
+template <int EPI, int WR, int WC, int RB, int CB, int SW, int MINB>
+__global__ void __launch_bounds__(256, MINB)
     gemm_mfma_kernel(const uint64_t *__restrict__ xp, const uint64_t *__restrict__ wp,
                      const EpiParams ep, void *__restrict__ yv, int M, int N, int K, int kw,
-                     int tiles_n) {
+                     int tiles_m, int tiles_n) {
   static_assert(WR * WC == 4, "4 waves per block");
   static_assert(!is_repack(EPI) || CB % 2 == 0, "repack pairs 32-column tiles");
+  static_assert(SW == 4 || SW == 8, "two or four words per lane per step");
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
+  constexpr int kSW = SW, kHW = SW / 2;  // words per step, per lane
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - (blockIdx.x / tiles_n) * tiles_n;
-  const int m0 = tm * BM + (wave / WC) * (RB * 32);
-  const int n0 = tn * BN + (wave % WC) * (CB * 32);
-  const int h = lane >> 5;    // which word pair of a 4-word step
+
+  // XCD-aware tile order (column-tile major: consecutive tiles share W).
+  // Grids that are not a multiple of 8 keep the plain order past the last
+  // whole group of 8.
+  const int T = tiles_m * tiles_n;
+  const int per = T >> 3;
+  const int b = blockIdx.x;
+  const int tile = b < (per << 3) ? (b & 7) * per + (b >> 3) : b;
+  const int tn = tile / tiles_m, tm = tile - tn * tiles_m;
+  const int mb = tm * BM, nb = tn * BN;  // block origin
+  const int m0 = mb + (wave / WC) * (RB * 32);
+  const int n0 = nb + (wave % WC) * (CB * 32);
+  const int h = lane >> 5;    // which half of a step's words
   const int li = lane & 31;   // row / column within a 32 x 32 tile
 
-  // Row / column pointers, clamped into the matrices (rows past M and
-  // columns past N compute garbage that is never stored).
-  const uint64_t *arow[RB];
-  const uint64_t *bcol[CB];
+  // Buffer resources over the block's rows of X and W: offsets are relative
+  // to the block origin and the extent is exactly the rows that exist, so
+  // every load past them returns 0.
+  const int rows_a = (M - mb) < BM ? (M - mb) : BM;
+  const int rows_b = (N - nb) < BN ? (N - nb) : BN;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint64_t *>(xp + (int64_t)mb * kw), (short)0, rows_a * kw * 8, 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint64_t *>(wp + (int64_t)nb * kw), (short)0, rows_b * kw * 8, 0x00020000);
+  uint32_t aoff[RB], boff[CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    int m = m0 + rb * 32 + li;
-    m = m < M ? m : M - 1;
-    arow[rb] = xp + (int64_t)m * kw;
+    int r = m0 - mb + rb * 32 + li;
+    r = r < rows_a ? r : rows_a - 1;  // rows past M compute garbage that is never stored
+    aoff[rb] = (uint32_t)(r * kw * 8 + h * (kHW * 8));
   }
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    int n = n0 + cb * 32 + li;
-    n = n < N ? n : N - 1;
-    bcol[cb] = wp + (int64_t)n * kw;
+    int c = n0 - nb + cb * 32 + li;
+    c = c < rows_b ? c : rows_b - 1;
+    boff[cb] = (uint32_t)(c * kw * 8 + h * (kHW * 8));
   }
 
   // Per-column epilogue operands, fetched before the K loop: the scale, or
@@ -119,105 +179,126 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  // Steps of kSW = 8 words (512 elements of K): lanes 0-31 hold words
-  // k0 .. k0+3 of their row / column, lanes 32-63 words k0+4 .. k0+7; slice
-  // q (0..7) pairs half (q & 1) of word (q >> 1) of both lane halves.  A step
-  // is "clean" when all its elements are inside K; only the last step can
-  // be partial.
-  constexpr int kSW = BNN_MFMA_SW, kHW = kSW / 2;
   const int nsteps = (kw + kSW - 1) / kSW;
-  const int nclean = (K >> 6) / kSW;
-
+  const int nclean = (K >> 6) / kSW;  // steps with every element inside K
   const uint32_t c8 = 0x88888888u, c2 = 0x22222222u;
-  typedef uint64_t ABuf[RB][kHW];
-  typedef uint64_t BBuf[CB][kHW];
-  auto load_clean = [&](int s, ABuf &a, BBuf &b) {
-    const int w = s * kSW + kHW * h;
+
+  // Step registers: 32-bit chunks, [operand][chunk] with chunk 2i + q = half
+  // q of this lane's word i.
+  typedef uint32_t ABuf[RB][2 * kHW];
+  typedef uint32_t BBuf[CB][2 * kHW];
+  auto load_step = [&](int s, ABuf &a, BBuf &bb) __attribute__((always_inline)) {
+    const int so = s * (kSW * 8);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < kHW; ++i) a[rb][i] = arow[rb][w + i];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int i = 0; i < kHW; ++i) b[cb][i] = bcol[cb][w + i];
-  };
-  auto mma_step = [&](const ABuf &a, const BBuf &b, bool masked, int s) {
-    // word i of this lane's half feeds slices 2i (low 32) and 2i+1 (high 32)
-#pragma unroll
-    for (int i = 0; i < kHW; ++i) {
-      v8i ao[2][RB], bo[2][CB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) fp4_operands(a[rb][i], c8, c2, ao[0][rb], ao[1][rb]);
-      if (masked) {
-        const int64_t e = (int64_t)(s * kSW + kHW * h + i) * 64;
-        const uint32_t v0 = valid_bits(e, K), v1 = valid_bits(e + 32, K);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          ao[0][rb] = mask_operand(ao[0][rb], v0);
-          ao[1][rb] = mask_operand(ao[1][rb], v1);
-        }
+      for (int j = 0; j < kHW / 2; ++j) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[rb] + 16 * j, so, 0);
+        a[rb][4 * j + 0] = v.x; a[rb][4 * j + 1] = v.y;
+        a[rb][4 * j + 2] = v.z; a[rb][4 * j + 3] = v.w;
       }
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) fp4_operands(b[cb][i], c8, c2, bo[0][cb], bo[1][cb]);
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                ao[q][rb], bo[q][cb], acc[rb][cb], kFmtFp4, kFmtFp4, 0, kScaleOne, 0, kScaleOne);
-    }
-#if BNN_MFMA_SCHED
-    // Interleave: one MFMA, then a few VALU ops (the next word's unpack).
-#pragma unroll
-    for (int j = 0; j < kHW * 2 * RB * CB; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, BNN_MFMA_SCHED, 0);
-    }
-#endif
+      for (int j = 0; j < kHW / 2; ++j) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bres, boff[cb] + 16 * j, so, 0);
+        bb[cb][4 * j + 0] = v.x; bb[cb][4 * j + 1] = v.y;
+        bb[cb][4 * j + 2] = v.z; bb[cb][4 * j + 3] = v.w;
+      }
   };
-
-  // Two register buffers in ping-pong: the loads of step s+1 are in flight
-  // while step s runs.  A scheduling barrier keeps each prefetch ahead of the
-  // MFMAs it is meant to overlap (left alone, the scheduler sinks the loads
-  // behind most of the step, and the loop head then waits for every load).  Both halves of the pair loop are unconditional (a
-  // conditional use would let the compiler sink the prefetch behind the
-  // MFMAs); the load past the last clean step re-reads that step (clamped,
-  // in bounds, unused).  An odd last step runs after the loop.
-  ABuf a0, a1;
-  BBuf b0, b1;
-  if (nclean > 0) load_clean(0, a0, b0);
-  int s = 0;
-  for (; s + 1 < nclean; s += 2) {
-    load_clean(s + 1, a1, b1);
-#if BNN_MFMA_PIN
-    __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the MFMAs
-#endif
-    mma_step(a0, b0, false, s);
-    load_clean(s + 2 < nclean ? s + 2 : nclean - 1, a0, b0);
-#if BNN_MFMA_PIN
-    __builtin_amdgcn_sched_barrier(0);
-#endif
-    mma_step(a1, b1, false, s + 1);
-  }
-  if (s < nclean) mma_step(a0, b0, false, s);
-  if (nclean < nsteps) {  // the partial last step: guarded loads, masked A
-    const int w = nclean * kSW + kHW * h;
+  // Slices.  Slice j of a step (j = 2i + q: half q of this lane's word i)
+  // unpacks RB + CB operand sets and feeds RB * CB MFMAs.  The slices run as
+  // a software pipeline: while the MFMAs of slice j issue, the VALU unpacks
+  // slice j + 1 (of the next step after a step's last slice) into the other
+  // of two operand register sets, interleaved one MFMA to three or four
+  // VALU ops (the matrix unit and the VALU then work side by side in one
+  // wave instead of in turns).
+  struct Ops {
+    v4i a[RB], b[CB];
+  };
+  Ops op0, op1;
+  auto unpack = [&](const ABuf &a, const BBuf &bb, int j, Ops &o, bool masked, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) o.a[rb] = fp4_chunk(a[rb][j], c8, c2);
+    if (masked) {
+      const int64_t e = (int64_t)(s * kSW + kHW * h + (j >> 1)) * 64 + 32 * (j & 1);
+      const uint32_t v = valid_bits(e, K);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o.a[rb] = mask4(o.a[rb], v);
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o.b[cb] = fp4_chunk(bb[cb][j], c8, c2);
+  };
+  auto mfmas = [&](const Ops &o) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < kHW; ++i) a0[rb][i] = w + i < kw ? arow[rb][w + i] : 0;
+      for (int cb = 0; cb < CB; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fp4_operand(o.a[rb]), fp4_operand(o.b[cb]), acc[rb][cb], kFmtFp4, kFmtFp4, 0,
+            kScaleOne, 0, kScaleOne);
+  };
+  // One MFMA, then 7 (RB + CB) / (RB CB) VALU ops on average, for every
+  // MFMA of a slice.
+  auto interleave = [&]() __attribute__((always_inline)) { interleave_groups<0, RB * CB, 7 * (RB + CB)>(); };
+  // A clean step whose slice-0 operands are already in set 0: slices 1.. of
+  // (a, bb), and slice 0 of the following step (an, bn).
+  auto run_step = [&](const ABuf &a, const BBuf &bb, const ABuf &an, const BBuf &bn) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int j = 0; j < 2 * kHW; j += 2) {
+      unpack(a, bb, j + 1, op1, false, 0);
+      mfmas(op0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // the next step's first slice (unused after the last step: its
+      // registers then hold a re-read step)
+      if (j + 2 < 2 * kHW)
+        unpack(a, bb, j + 2, op0, false, 0);
+      else
+        unpack(an, bn, 0, op0, false, 0);
+      mfmas(op1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Two step register sets in ping-pong: the loads of step s+1 are issued
+  // at the start of step s (a scheduling barrier keeps them there), and its
+  // first slice is unpacked during step s's last one.  The loop runs whole
+  // pairs of clean steps; the load past the last pair re-reads its second
+  // step (in bounds, unused).  What is left -- an odd clean step and the
+  // partial last step (K not a multiple of 64 * SW) -- runs after the loop
+  // one slice at a time with the pad elements masked in A (a clean step's
+  // mask keeps every element).
+  ABuf a0, a1;
+  BBuf b0, b1;
+  const int npair = nclean >> 1;
+  if (npair > 0) {
+    load_step(0, a0, b0);
+    unpack(a0, b0, 0, op0, false, 0);
+    for (int s = 0; s < 2 * npair; s += 2) {
+      load_step(s + 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      run_step(a0, b0, a1, b1);
+      load_step(s + 2 < 2 * npair ? s + 2 : s + 1, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      run_step(a1, b1, a0, b0);
+    }
+  }
+  for (int s = 2 * npair; s < nsteps; ++s) {
+    load_step(s, a0, b0);  // words past K: garbage (masked) or 0 (past the rows)
 #pragma unroll
-      for (int i = 0; i < kHW; ++i) b0[cb][i] = w + i < kw ? bcol[cb][w + i] : 0;
-    mma_step(a0, b0, true, nclean);
+    for (int j = 0; j < 2 * kHW; ++j) {
+      unpack(a0, b0, j, op0, true, s);
+      mfmas(op0);
+    }
   }
 
   // Epilogue.  acc[rb][cb][v] is the exact integer dot of row
   // m0 + rb*32 + 8(v/4) + 4h + v%4 and column n0 + cb*32 + li.
+  // Every load is waited for once here (the scales were loaded before the K
+  // loop and the last prefetch re-read a step), so that no store below waits.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   if (is_repack(EPI)) {
     const int nw = (N + 63) >> 6;
 #pragma unroll
@@ -241,8 +322,9 @@ __global__ void __launch_bounds__(256)
         }
       }
   } else {
-    // Row r(v) = 8 (v / 4) + v % 4 of a 32-row tile (plus 4h): four row
-    // pointers, stepped by 8 rows.  Tiles wholly inside M skip the row test.
+    // Row r(v) = 8 (v / 4) + v % 4 of a 32-row tile (plus 4h).  Tiles wholly
+    // inside M store their 16 values without a row test (straight-line
+    // stores: no branch per value).
     const int64_t ld = N;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -253,35 +335,39 @@ __global__ void __launch_bounds__(256)
         const int n = n0 + cb * 32 + li;
         if (n >= N) continue;
         const float a = a_pre[cb];
-        if (EPI == BNN_EPI_I32) {
-          int32_t *p = static_cast<int32_t *>(yv) + (int64_t)mt * ld + n;
+        const int64_t base = (int64_t)mt * ld + n;
+        auto put = [&](int v) __attribute__((always_inline)) {
+          // (8 (v / 4) + v % 4) * ld is the same for every lane
+          const int64_t o = base + (int64_t)(8 * (v >> 2) + (v & 3)) * ld;
+          if (EPI == BNN_EPI_I32)
+            static_cast<int32_t *>(yv)[o] = (int)acc[rb][cb][v];
+          else
+            static_cast<float *>(yv)[o] = __fmul_rn(acc[rb][cb][v], a);
+        };
+        if (full_rows) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int dr = 8 * (v >> 2) + (v & 3);
-            if (full_rows || mt + dr < M) p[dr * ld] = (int)acc[rb][cb][v];
-          }
+          for (int v = 0; v < 16; ++v) put(v);
         } else {
-          float *p = static_cast<float *>(yv) + (int64_t)mt * ld + n;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int dr = 8 * (v >> 2) + (v & 3);
-            if (full_rows || mt + dr < M) p[dr * ld] = __fmul_rn(acc[rb][cb][v], a);
-          }
+          for (int v = 0; v < 16; ++v)
+            if (mt + 8 * (v >> 2) + (v & 3) < M) put(v);
         }
       }
     }
   }
 }
 
-template <int EPI, int WR, int WC, int RB, int CB>
+template <int EPI, int WR, int WC, int RB, int CB, int SW, int MINB>
 hipError_t launch_cfg(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y, int M,
                       int N, int K, hipStream_t s) {
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
   const int kw = (K + 63) / 64;
+  const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  const int64_t tiles = (int64_t)((M + BM - 1) / BM) * tiles_n;
-  hipLaunchKernelGGL((gemm_mfma_kernel<EPI, WR, WC, RB, CB>), dim3((unsigned)tiles), dim3(256), 0,
-                     s, xp, wp, ep, y, M, N, K, kw, tiles_n);
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  hipLaunchKernelGGL((gemm_mfma_kernel<EPI, WR, WC, RB, CB, SW, MINB>), dim3((unsigned)tiles),
+                     dim3(256), 0,
+                     s, xp, wp, ep, y, M, N, K, kw, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -289,9 +375,13 @@ template <int EPI>
 hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y, int M,
                       int N, int K, hipStream_t s) {
   // Narrow outputs stack the four waves along M so that no wave idles.
-  if (N <= 64) return launch_cfg<EPI, 4, 1, 1, 2>(xp, wp, ep, y, M, N, K, s);  // 128 x 64
-  return launch_cfg<EPI, BNN_MFMA_WR, BNN_MFMA_WC, BNN_MFMA_RB, BNN_MFMA_CB>(xp, wp, ep, y, M, N, K,
-                                                                          s);
+  if (N <= 64) return launch_cfg<EPI, 4, 1, 1, 2, 8, 2>(xp, wp, ep, y, M, N, K, s);  // 128 x 64
+  // Large products: 256 x 256 block tiles of 4 x 4 wave tiles, while they
+  // still give every CU at least one block and K is long enough for the K
+  // loop (not the epilogue) to dominate a tile.
+  const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  if (big >= 256 && K >= 2048) return launch_cfg<EPI, BNN_MFMA_BIG>(xp, wp, ep, y, M, N, K, s);
+  return launch_cfg<EPI, 4, 1, 2, 2, 8, 2>(xp, wp, ep, y, M, N, K, s);  // 256 x 64
 }
 
 }  // namespace

@@ -134,6 +134,8 @@ __global__ void __launch_bounds__(256)
   }
 
   // Epilogue: <x, w> = K - 2d (computed mod 2^32; the true value fits int32).
+  // Nothing is left in flight, so that no store below waits.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   const int nw = (N + 63) >> 6;
 #pragma unroll
   for (int c = 0; c < kColsPerLane; ++c) {

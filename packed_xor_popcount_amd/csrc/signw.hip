@@ -496,6 +496,9 @@ __global__ void __launch_bounds__(256, MINB)
     compute(as[0], wa);
   }
 
+  // Nothing is left in flight, so that no store below waits; tiles wholly
+  // inside M store without a row test (straight-line stores).
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   const int64_t ld = N;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -506,11 +509,17 @@ __global__ void __launch_bounds__(256, MINB)
       const int n = n0 + cb * 32 + li;
       if (n >= N) continue;
       float *p = y + (int64_t)mt * ld + n;
+      auto put = [&](int v) __attribute__((always_inline)) {
+        p[(int64_t)(8 * (v >> 2) + (v & 3)) * ld] =
+            SCALED ? __fmul_rn(acc[rb][cb][v], a_pre[cb]) : acc[rb][cb][v];
+      };
+      if (full_rows) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int dr = 8 * (v >> 2) + (v & 3);
-        if (full_rows || mt + dr < M)
-          p[dr * ld] = SCALED ? __fmul_rn(acc[rb][cb][v], a_pre[cb]) : acc[rb][cb][v];
+        for (int v = 0; v < 16; ++v) put(v);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (mt + 8 * (v >> 2) + (v & 3) < M) put(v);
       }
     }
   }

@@ -148,6 +148,46 @@ def test_gemm_all_epilogues(M, N, K, algo):
     assert np.array_equal(gotp, refp)
 
 
+@pytest.mark.parametrize("K", [1000, 2049, 2304, 4163])
+def test_mfma_large_tiles_ragged(K):
+    # Large products with K >= 2048 run 256 x 256 block tiles of 4 x 4 wave
+    # tiles on the matrix cores (K = 2049: a partial last step; 2304: an odd
+    # number of whole steps; 4163: both), shorter K the 256 x 64 tiles:
+    # ragged M, N and K past every tile edge, garbage pad bits; the ragged
+    # block row and block column are compared in full, the rest on sampled
+    # outputs, for every epilogue.
+    M, N = 16 * 256 + 37, 16 * 256 + 45
+    say("mfma large tiles", M, N, K)
+    rng = np.random.default_rng(K + 17)
+    xg, xc = rand_packed(rng, M, K)
+    wg, wc = rand_packed(rng, N, K)
+    alpha = (rng.standard_normal(N) * 3).astype(np.float32)
+    alpha[::5] = 0.0
+    xd, wd, ad = to_dev_words(xg), to_dev_words(wg), torch.from_numpy(alpha).to(DEV)
+    yi = bnn.gemm_ex(xd, wd, K, bnn.EPI_I32, bnn.ALGO_MFMA).cpu().numpy()
+    ys = bnn.gemm_ex(xd, wd, K, bnn.EPI_SCALED, bnn.ALGO_MFMA, alpha=ad).cpu().numpy()
+    yp = words_np(bnn.gemm_ex(xd, wd, K, bnn.EPI_REPACK, bnn.ALGO_MFMA))
+    thr = rand_thr(rng, N, K)
+    mask = rng.integers(0, 2 ** 64, size=oracle.words(N), dtype=np.uint64)
+    yt = words_np(bnn.gemm_sign_repack_thr(xd, wd, torch.from_numpy(thr).to(DEV), K,
+                                           to_dev_words(mask[None])[0], bnn.ALGO_MFMA))
+    edge_r = np.arange(4096, M)
+    edge_c = np.arange(4096, N)
+    some_r = np.sort(rng.choice(4096, 40, replace=False))
+    rows = np.concatenate([some_r, edge_r])
+    ref_rows = oracle.gemm_i32(xc[rows], wc, K)
+    assert np.array_equal(yi[rows], ref_rows)
+    assert_scaled_equal(ys[rows], oracle.gemm_scaled(xc[rows], wc, alpha, K))
+    assert np.array_equal(yp[rows], oracle.sign_repack(xc[rows], wc, K))
+    assert np.array_equal(yt[rows], oracle.sign_repack_thr(xc[rows], wc, thr, K,
+                                                           flags_of(mask, N)))
+    ref_cols = oracle.gemm_i32(xc, wc[edge_c], K)
+    assert np.array_equal(yi[:, edge_c], ref_cols)
+    assert_scaled_equal(ys[:, edge_c], oracle.gemm_scaled(xc, wc[edge_c], alpha[edge_c], K))
+    mi, ni = _sample_pairs(rng, M, N, 20000)
+    assert np.array_equal(yi[mi, ni], oracle.dot_pairs(xc, wc, K, mi, ni))
+
+
 def test_named_entry_points_match_oracle():
     rng = np.random.default_rng(5)
     for M, N, K in [(1, 777, 1000), (200, 300, 700)]:
@@ -429,6 +469,36 @@ def test_gemv_act_parity(M, N, K, dtype):
     alpha = c["alpha"]
     xd, wd, ad = x.to(DEV), to_dev_words(wg), alpha.to(DEV)
     rx = oracle.pack(host_input(x), k=K) if M else np.zeros((0, oracle.words(K)), np.uint64)
+    assert np.array_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_I32).cpu().numpy(),
+                          oracle.gemm_i32(rx, wc, K))
+    assert_scaled_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_SCALED, alpha=ad).cpu().numpy(),
+                        oracle.gemm_scaled(rx, wc, alpha.numpy(), K))
+    assert np.array_equal(words_np(bnn.gemv_act(xd, wd, K, bnn.EPI_REPACK)),
+                          oracle.sign_repack(rx, wc, K))
+
+
+@pytest.mark.parametrize("M", [2, 5, 8])
+@pytest.mark.parametrize("K", [512, 4096])
+@pytest.mark.parametrize("pad", [0, 1])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gemv_act_several_rows(M, K, pad, dtype):
+    # the straight-line batch form with 2..8 rows: each row's words in LDS,
+    # rows contiguous (pad 0) or with a padded stride that keeps every row
+    # start 16-byte aligned (pad 1)
+    N = 77 + 1000 * (K == 512)
+    say("gemv_act rows", M, K, pad, dtype, N)
+    esize = 4 if dtype == torch.float32 else 2
+    ld = K + pad * (16 // esize)
+    c = workloads.random_case(seed=M * 131 + K + pad, M=M, N=N, K=ld, dist="normal",
+                              zero_frac=0.01, dtype=dtype)
+    big = c["x"]
+    rng = np.random.default_rng(M + K + pad)
+    wg, wc = rand_packed(rng, N, K)
+    alpha = c["alpha"][:N]
+    xd = big.to(DEV)[:, :K]
+    assert xd.stride(0) == ld and (ld * esize) % 16 == 0
+    wd, ad = to_dev_words(wg), alpha.to(DEV)
+    rx = oracle.pack(np.ascontiguousarray(host_input(big)[:, :K]))
     assert np.array_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_I32).cpu().numpy(),
                           oracle.gemm_i32(rx, wc, K))
     assert_scaled_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_SCALED, alpha=ad).cpu().numpy(),
