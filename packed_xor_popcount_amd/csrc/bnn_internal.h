@@ -104,6 +104,20 @@ constexpr int kWave = 64;  // CDNA wavefront width
 // losing track of such loads across the stores' branches, would otherwise
 // wait for every earlier store before each new one.
 constexpr int kWaitVmem0 = 0x0F70;
+
+// A copy of a loaded value that the compiler treats as computed at this
+// point: taking it waits for the load once (for exactly that load), and
+// later uses of the copy -- inside loops, behind branches -- need no wait
+// on vector memory, so they never drain loads or stores issued after it.
+// Register-only.
+__device__ __forceinline__ uint32_t settled(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+__device__ __forceinline__ uint64_t settled(uint64_t v) {
+  return (uint64_t)settled((uint32_t)v) | ((uint64_t)settled((uint32_t)(v >> 32)) << 32);
+}
 constexpr int64_t kMfmaMaxK = int64_t(1) << 24;  // fp32 accumulation of +-1 is exact up to here
 
 // acc + popcount(v) as the single accumulate form of v_bcnt_u32_b32.  Written

@@ -274,18 +274,23 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// Batch-1 decode form of the fused kernel: activation rows given as real
-// values (M <= 8, DT 0 = fp32, 1 = bf16, K a multiple of 64, rows 16-byte
-// aligned), and every lane holds at most one unit (VEC words) of each W row
-// it serves (units <= L), so a block step is
-// one straight-line round: issue the scale loads, the activation loads
-// (first step of the block only), then the W loads; pack the activations
-// into LDS while the W words are in flight; popcounts; reduction; epilogue.  The
-// same arithmetic and epilogues as gemv_kernel.
-template <int EPI, int L, int VEC, int P, int DT>
+// Batch decode form (M <= 8): every lane holds at most one unit (VEC words)
+// of each W row it serves (units <= L), so a block step is one
+// straight-line round: issue the scale loads, the activation loads (first
+// step of the block only), then the W loads; popcounts; reduction;
+// epilogue.  The same arithmetic and epilogues as gemv_kernel.  XT 1 / 2:
+// activation rows given as real fp32 / bf16 values (K a multiple of 64,
+// rows 16-byte aligned), packed into LDS while the first W words are in
+// flight.  XT 0: packed activation rows (the named products at small M);
+// a lane's activation words are the same for every step, so they are
+// loaded into registers once.  TAIL (XT 0 only): K is not a multiple of 64
+// and the last word's pad bits are masked.
+template <int EPI, int L, int VEC, int P, int XT, bool TAIL>
 __global__ void __launch_bounds__(256)
     gemv_act_kernel(const void *__restrict__ xv, int64_t ldx, const uint64_t *__restrict__ wp,
                     const EpiParams ep, void *__restrict__ yv, int M, int N, int K, int kw) {
+  constexpr int DT = XT == 2 ? 1 : 0;
+  static_assert(!TAIL || XT == 0, "real-valued rows hold whole words");
   constexpr int G = 64 / L;
   constexpr int CB = 4 * G * P;
   constexpr int kS = 4;  // activation words per lane group per round
@@ -305,6 +310,28 @@ __global__ void __launch_bounds__(256)
   const bool u_ok = part < units;
   const int u = u_ok ? part : units - 1;
   const int total = M * kw;     // activation words to pack
+
+  // XT 0: this lane's activation words (unit u of every row), masked past
+  // K in the last word, loaded once.
+  uint64_t xw[kMR][VEC];
+  if constexpr (XT == 0) {
+    const uint64_t *xp = static_cast<const uint64_t *>(xv);
+#pragma unroll
+    for (int rr = 0; rr < kMR; ++rr) {
+      if (rr >= M) break;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        const int word = u * VEC + v;
+        uint64_t x = xp[(int64_t)rr * ldx + word];
+        if (TAIL && word == kw - 1) x &= tail_mask(K);
+        xw[rr][v] = x;
+      }
+    }
+  }
+  // Pad-bit mask of this lane's words (TAIL): W's pad bits must not count.
+  uint64_t wmask[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) wmask[v] = (TAIL && u * VEC + v == kw - 1) ? tail_mask(K) : ~0ull;
 
   // Every activation row holds whole 16-byte-aligned groups of 8 elements
   // (the launcher checks this), so the loads are unconditional vector loads;
@@ -388,17 +415,22 @@ __global__ void __launch_bounds__(256)
     for (int p = 0; p < P; ++p)
 #pragma unroll
       for (int rr = 0; rr < kMR; ++rr) acc[p][rr] = 0;
-    if (u_ok) {  // K is a multiple of 64: no tail word to mask
+    if (u_ok) {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
         const int word = u * VEC + v;
 #pragma unroll
         for (int rr = 0; rr < kMR; ++rr) {
           if (rr >= M) break;
-          const uint64_t x = xs[rr * kw + word];
+          uint64_t x;
+          if constexpr (XT == 0)
+            x = xw[rr][v];
+          else
+            x = xs[rr * kw + word];
 #pragma unroll
           for (int p = 0; p < P; ++p) {
-            const uint64_t d = x ^ r.w[p][v];
+            uint64_t d = x ^ r.w[p][v];
+            if (TAIL) d &= wmask[v];
             acc[p][rr] = popc_acc((uint32_t)(d >> 32), popc_acc((uint32_t)d, acc[p][rr]));
           }
         }
@@ -458,23 +490,42 @@ __global__ void __launch_bounds__(256)
   // steps stream W continuously); a pair's second half exists only when the
   // block has that step, so single-step blocks load nothing extra.  The two
   // register sets are never copied (a copy would wait for its load).
-  Raw8 raw[kS];
-  x_round(0, raw);
   StepRegs ra;
-  load_step(blockIdx.x, ra);
-  x_store(0, raw);
-  for (int q0 = 32 * kS; q0 < total; q0 += 32 * kS) {
-    x_round(q0, raw);
-    x_store(q0, raw);
+  if constexpr (XT != 0) {
+    Raw8 raw[kS];
+    x_round(0, raw);
+    load_step(blockIdx.x, ra);
+    x_store(0, raw);
+    for (int q0 = 32 * kS; q0 < total; q0 += 32 * kS) {
+      x_round(q0, raw);
+      x_store(q0, raw);
+    }
+    __syncthreads();
+  } else {
+    load_step(blockIdx.x, ra);
+    // the activation words are settled once, behind the first W loads
+#pragma unroll
+    for (int rr = 0; rr < kMR; ++rr) {
+      if (rr >= M) break;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) xw[rr][v] = settled(xw[rr][v]);
+    }
   }
-  __syncthreads();
+  // A block with one step (the batch-1 sizes) runs it and ends.  Otherwise
+  // the prefetches are unconditional -- past the block's last step they
+  // re-read its current step -- so that the compiler's count of loads in
+  // flight is exact and each step waits for its own loads only.
+  if (blockIdx.x + gridDim.x >= nsteps) {
+    run_step(blockIdx.x, ra);
+    return;
+  }
   for (int step = blockIdx.x; step < nsteps; step += 2 * gridDim.x) {
     const int sb = step + gridDim.x, sa = step + 2 * gridDim.x;
     StepRegs rb;
-    if (sb < nsteps) load_step(sb, rb);  // uniform
+    load_step(sb < nsteps ? sb : step, rb);
     run_step(step, ra);
-    if (sa < nsteps) load_step(sa, ra);
-    if (sb < nsteps) run_step(sb, rb);
+    load_step(sa < nsteps ? sa : step, ra);
+    if (sb < nsteps) run_step(sb, rb);  // uniform
   }
 }
 
@@ -496,13 +547,25 @@ hipError_t launch_lp(const Args &a, hipStream_t s) {
   const int64_t cap = 256 * kBlocksPerCU;
   const int64_t blocks = steps < cap ? steps : cap;
   const int rows = a.M < kMR ? a.M : kMR;
-  if constexpr (XT != 0) {
-    // Batch-1 decode form: at most 8 rows and at most one unit per lane.
-    if (a.M <= kMR && a.kw > 0 && a.kw / VEC <= L && a.K % 64 == 0 && a.xvec) {
-      const size_t shmem = (size_t)a.M * a.kw * sizeof(uint64_t);
-      hipLaunchKernelGGL((gemv_act_kernel<EPI, L, VEC, P, XT - 1>), dim3((unsigned)blocks),
-                         dim3(256), shmem, s, a.x, a.ldx, a.wp, a.ep, a.y, a.M, a.N, a.K,
-                         a.kw);
+  // Batch decode form: at most 8 rows and at most one unit per lane; real
+  // rows hold whole 16-byte-aligned words, packed rows may end in a partial
+  // word.
+  if (a.M <= kMR && a.kw > 0 && a.kw / VEC <= L) {
+    if constexpr (XT != 0) {
+      if (a.K % 64 == 0 && a.xvec) {
+        const size_t shmem = (size_t)a.M * a.kw * sizeof(uint64_t);
+        hipLaunchKernelGGL((gemv_act_kernel<EPI, L, VEC, P, XT, false>), dim3((unsigned)blocks),
+                           dim3(256), shmem, s, a.x, a.ldx, a.wp, a.ep, a.y, a.M, a.N, a.K,
+                           a.kw);
+        return hipGetLastError();
+      }
+    } else {
+      if (a.K % 64 == 0)
+        hipLaunchKernelGGL((gemv_act_kernel<EPI, L, VEC, P, 0, false>), dim3((unsigned)blocks),
+                           dim3(256), 0, s, a.x, a.ldx, a.wp, a.ep, a.y, a.M, a.N, a.K, a.kw);
+      else
+        hipLaunchKernelGGL((gemv_act_kernel<EPI, L, VEC, P, 0, true>), dim3((unsigned)blocks),
+                           dim3(256), 0, s, a.x, a.ldx, a.wp, a.ep, a.y, a.M, a.N, a.K, a.kw);
       return hipGetLastError();
     }
   }
