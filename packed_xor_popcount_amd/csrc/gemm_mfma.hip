@@ -26,22 +26,23 @@
 //    nothing whatever the pad bits of either operand hold.
 //
 // Work split.  A block is 4 waves arranged WR x WC; a wave owns RB x CB
-// tiles of 32 x 32 outputs.  The unpack costs 7 VALU ops per operand
-// register set and one set feeds CB (A) or RB (B) MFMAs of 32 cycles, so
-// VALU per MFMA = 7 (RB + CB) / (RB CB): 3.5 at 4 x 4 tiles, where the
-// matrix cores (not the VALU) set the pace.  The large configuration is
-// therefore 2 x 2 waves of 4 x 4 tiles (block tile 256 x 256, one wave per
-// SIMD, accumulators in the AGPRs); small shapes use 4 x 1 waves of 2 x 2.
+// tiles of 32 x 32 outputs.  The unpack costs 5.5 VALU ops per operand
+// register set (the two 32-element halves of a word share their 64-bit
+// shifts) and one set feeds CB (A) or RB (B) MFMAs of 32 cycles, so VALU
+// per MFMA = 5.5 (RB + CB) / (RB CB): 2.75 at 4 x 4 tiles.  The large
+// configuration is therefore 2 x 2 waves of 4 x 4 tiles (block tile
+// 256 x 256, one wave per SIMD, accumulators in the AGPRs); small shapes use
+// 4 x 1 waves of 1 x 2 or 2 x 2.
 //
-// K loop.  A step is 8 words (512 elements of K): lanes 0-31 hold words
-// 8s .. 8s+3 of their row / column, lanes 32-63 words 8s+4 .. 8s+7; slice
-// (i, q) pairs half q of word i of both lane halves.  The words are read
-// with buffer loads through per-block resources: each lane's row offset is
-// fixed and the step offset is a scalar, so a step costs no vector address
-// arithmetic, and every load outside the block's rows returns 0 (no load
-// can leave the matrices).  Two register sets ping-pong: step s+1 is in
-// flight while step s runs.  Inside a step, slice j+1 is unpacked while
-// slice j's MFMAs run.
+// K loop.  A step is SW words (64 SW elements of K): lanes 0-31 hold the
+// first SW / 2 words of the step of their row / column, lanes 32-63 the
+// last SW / 2; slice (i, q) pairs half q of word i of both lane halves.  The
+// words are read with buffer loads through per-block resources: each
+// lane's row offset is fixed and the step offset is a scalar, so a step
+// costs no vector address arithmetic, and every load outside the block's
+// rows returns 0 (no load can leave the matrices).  Two register sets
+// ping-pong: step s+1 is in flight while step s runs.  Inside a step, slice
+// j+1 is unpacked while slice j's MFMAs run.
 //
 // Tile order.  Hardware places block b on XCD b % 8; block b takes logical
 // tile (b % 8) * (T / 8) + b / 8 (T tiles, column-tile major), so each
@@ -60,11 +61,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Large-product configuration (waves WR x WC, wave tiles RB x CB, words of
-// K per step, blocks per CU the register allocation must allow).
-#ifndef BNN_MFMA_BIG
-#define BNN_MFMA_BIG 2, 2, 4, 4, 4, 1
-#endif
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -77,6 +73,19 @@ __device__ __forceinline__ v4i fp4_chunk(uint32_t c, uint32_t c8, uint32_t c2) {
   o[2] = (int)and_or(c << 1, c8, c2);
   o[3] = (int)and_or(c, c8, c2);
   return o;
+}
+
+// w << s as one v_lshlrev_b64 (the compiler splits a 64-bit shift whose
+// halves are used apart into two 32-bit ops).  `pinned`: volatile, so that
+// the scheduler keeps it where it is written.
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t w, bool pinned) {
+  uint64_t r;
+  if (pinned)
+    asm volatile("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(w));
+  else
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(w));
+  return r;
 }
 
 // The eight-register operand of the FP4 MFMA: an FP4 operand uses the first
@@ -92,14 +101,256 @@ __device__ __forceinline__ v4i mask4(v4i a, uint32_t valid) {
   return (v4i){m[0], m[1], m[2], m[3]};
 }
 
-// Scheduling groups of one slice: NM MFMAs, each followed by its share of NV
-// VALU ops (the shares differ by at most one).
-template <int I, int NM, int NV>
-__device__ __forceinline__ void interleave_groups() {
-  if constexpr (I < NM) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, (NV * (I + 1)) / NM - (NV * I) / NM, 0);
-    interleave_groups<I + 1, NM, NV>();
+// Epilogue operands of the columns nc[cb] + li (li = lane % 32): the scale,
+// or the threshold as an fp32 bound that is exact against the (exact, |d| <=
+// K <= 2^24) accumulators -- +inf / -inf outside [-K, K] -- and the flip word
+// of each 64-column pair (nc[2cp], nc[2cp] + 32).  Loaded before the K loop.
+template <int EPI, int CB>
+__device__ __forceinline__ void epilogue_operands(const EpiParams &ep, const int (&nc)[CB], int li,
+                                                  int N, int K, float (&a_pre)[CB],
+                                                  uint64_t (&f_pre)[CB / 2 > 0 ? CB / 2 : 1]) {
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int n = nc[cb] + li;
+    a_pre[cb] = (EPI == BNN_EPI_SCALED && n < N) ? ep.alpha[n < N ? n : N - 1] : 0.0f;
+    if (EPI == kEpiRepackThr) {
+      const int32_t t = thr_of(ep, n, N);
+      a_pre[cb] = t >= K ? __builtin_inff() : (t < -K ? -__builtin_inff() : (float)t);
+    }
+  }
+#pragma unroll
+  for (int cp = 0; cp < (CB / 2 > 0 ? CB / 2 : 1); ++cp)
+    f_pre[cp] = (EPI == kEpiRepackThr && CB >= 2) ? flip_of(ep, nc[2 * cp] >> 6, N) : 0;
+}
+
+// Stores of RB x CB accumulator tiles: acc[rb][cb][v] is the exact integer
+// dot of row mr[rb] + 8 (v / 4) + 4h + v % 4 and column nc[cb] + li
+// (h = lane / 32, li = lane % 32); column pairs (2cp, 2cp + 1) are 64
+// consecutive columns starting at a multiple of 64.  Every load has been
+// waited for before this (so that no store waits).
+template <int EPI, int RB, int CB>
+__device__ __forceinline__ void store_tiles(const v16f (&acc)[RB][CB], const float (&a_pre)[CB],
+                                            const uint64_t (&f_pre)[CB / 2 > 0 ? CB / 2 : 1],
+                                            const int (&mr)[RB], const int (&nc)[CB], int h,
+                                            int li, void *__restrict__ yv, int M, int N) {
+  if (is_repack(EPI)) {
+    const int nw = (N + 63) >> 6;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cp = 0; cp < CB / 2; ++cp) {
+        const int na = nc[2 * cp] + li, nb2 = na + 32;
+        const int wi = nc[2 * cp] >> 6;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // bit set (-1) where the dot is <= the threshold (0 for the plain repack)
+          const uint64_t lo = __builtin_amdgcn_ballot_w64(na < N && acc[rb][2 * cp][v] <= a_pre[2 * cp]);
+          const uint64_t hi =
+              __builtin_amdgcn_ballot_w64(nb2 < N && acc[rb][2 * cp + 1][v] <= a_pre[2 * cp + 1]);
+          // lane 0 writes row r, lane 32 writes row r + 4
+          const int r = mr[rb] + 8 * (v >> 2) + (v & 3) + 4 * h;
+          const uint64_t word = (h ? ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32))
+                                   : ((hi << 32) | (lo & 0xFFFFFFFFull))) ^ f_pre[cp];
+          if (li == 0 && r < M && wi < nw) static_cast<uint64_t *>(yv)[(int64_t)r * nw + wi] = word;
+        }
+      }
+  } else {
+    // Tiles wholly inside M store their 16 values without a row test
+    // (straight-line stores: no branch per value).
+    const int64_t ld = N;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int mt = mr[rb] + 4 * h;  // row of v = 0 for this lane
+      const bool full_rows = mr[rb] + 32 <= M;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int n = nc[cb] + li;
+        if (n >= N) continue;
+        const float a = a_pre[cb];
+        const int64_t base = (int64_t)mt * ld + n;
+        auto put = [&](int v) __attribute__((always_inline)) {
+          // (8 (v / 4) + v % 4) * ld is the same for every lane
+          const int64_t o = base + (int64_t)(8 * (v >> 2) + (v & 3)) * ld;
+          if (EPI == BNN_EPI_I32)
+            static_cast<int32_t *>(yv)[o] = (int)acc[rb][cb][v];
+          else
+            static_cast<float *>(yv)[o] = __fmul_rn(acc[rb][cb][v], a);
+        };
+        if (full_rows) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) put(v);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (mt + 8 * (v >> 2) + (v & 3) < M) put(v);
+        }
+      }
+    }
+  }
+}
+
+// The K loop of one wave tile: acc[rb][cb] += the sum over K of the
+// products of A tile rb (the X rows at aoff[rb] in ares) and B tile cb (the
+// W rows at boff[cb] in bres).
+template <int RB, int CB, int SW>
+__device__ __forceinline__ void k_loop(v16f (&acc)[RB][CB], const __amdgpu_buffer_rsrc_t ares,
+                                       const __amdgpu_buffer_rsrc_t bres, const uint32_t (&aoff)[RB],
+                                       const uint32_t (&boff)[CB], int K, int kw, int h,
+                                       uint32_t c8, uint32_t c2) {
+  constexpr int kSW = SW, kHW = SW / 2;  // words per step, per lane
+  const int nsteps = (kw + kSW - 1) / kSW;
+  const int nclean = (K >> 6) / kSW;  // steps with every element inside K
+
+  // Operand sets: set p < RB is A tile p (rows), set RB + c is B tile c
+  // (columns).  Step registers: 32-bit chunks, [set][chunk] with chunk
+  // 2i + q = half q of this lane's word i.
+  constexpr int NS = RB + CB;
+  typedef uint32_t Buf[NS][2 * kHW];
+  auto load_step = [&](int s, Buf &u) __attribute__((always_inline)) {
+    const int so = s * (kSW * 8);
+#pragma unroll
+    for (int p = 0; p < NS; ++p)
+#pragma unroll
+      for (int j = 0; j < kHW / 2; ++j) {
+        const u32x4 v = p < RB
+                            ? __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[p] + 16 * j, so, 0)
+                            : __builtin_amdgcn_raw_buffer_load_b128(bres, boff[p - RB] + 16 * j, so, 0);
+        u[p][4 * j + 0] = v.x; u[p][4 * j + 1] = v.y;
+        u[p][4 * j + 2] = v.z; u[p][4 * j + 3] = v.w;
+      }
+  };
+  // Slices.  Slice j of a step (j = 2i + q: half q of this lane's word i)
+  // unpacks NS operand sets and feeds RB * CB MFMAs.  The slices run as a
+  // software pipeline: while the MFMAs of slice j issue, the VALU unpacks
+  // slice j + 1 (of the next step after a step's last slice) into the other
+  // of two operand register sets.  The two halves of a word share their
+  // shifts (as in fp4_operands): the even slice of word i takes the three
+  // 64-bit shifts of the word and keeps their high halves, the odd slice
+  // only masks those -- 5.5 instead of 7 VALU ops per set.  Each set's
+  // unpack is split in two work items, and the 2 NS items are placed
+  // between the MFMAs by hand (a scheduling barrier after each group), so
+  // that the VALU ops are spread evenly over the matrix-core instructions.
+  struct Ops {
+    v4i s[NS];
+  };
+  Ops op0, op1;
+  uint32_t keep[NS][3], lows[NS][3];
+  // Item k of set p for the even slice 2i.  `next`: a step register set
+  // whose loads may still be in flight; its shifts are then volatile, so
+  // that the wait for the loads stays here (the scheduler would otherwise
+  // pull the shifts up to the loads).
+  auto even_item = [&](const Buf &u, int i, Ops &o, bool next, int p, int k) __attribute__((always_inline)) {
+    if (k == 0) {
+      // the shifts, and the one register that needs none (no shift result
+      // is read right after it is written: that would cost a wait state)
+      const uint64_t w = ((uint64_t)u[p][2 * i + 1] << 32) | u[p][2 * i];
+      const uint64_t s1 = shl64<1>(w, next), s2 = shl64<2>(w, next), s3 = shl64<3>(w, next);
+      keep[p][0] = (uint32_t)(s3 >> 32);
+      keep[p][1] = (uint32_t)(s2 >> 32);
+      keep[p][2] = (uint32_t)(s1 >> 32);
+      lows[p][0] = (uint32_t)s3;
+      lows[p][1] = (uint32_t)s2;
+      lows[p][2] = (uint32_t)s1;
+      o.s[p][3] = (int)and_or(u[p][2 * i], c8, c2);
+    } else {
+      o.s[p][0] = (int)and_or(lows[p][0], c8, c2);
+      o.s[p][1] = (int)and_or(lows[p][1], c8, c2);
+      o.s[p][2] = (int)and_or(lows[p][2], c8, c2);
+    }
+  };
+  // Item k of set p for the odd slice 2i + 1, from the kept shifts.
+  auto odd_item = [&](const Buf &u, int i, Ops &o, int p, int k) __attribute__((always_inline)) {
+    if (k == 0) {
+      o.s[p][0] = (int)and_or(keep[p][0], c8, c2);
+      o.s[p][1] = (int)and_or(keep[p][1], c8, c2);
+    } else {
+      o.s[p][2] = (int)and_or(keep[p][2], c8, c2);
+      o.s[p][3] = (int)and_or(u[p][2 * i + 1], c8, c2);
+    }
+  };
+  auto mfma = [&](const Ops &o, int q) __attribute__((always_inline)) {
+    const int rb = q / CB, cb = q % CB;
+    acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        fp4_operand(o.s[rb]), fp4_operand(o.s[RB + cb]), acc[rb][cb], kFmtFp4, kFmtFp4, 0,
+        kScaleOne, 0, kScaleOne);
+  };
+  // The MFMAs of slice operands o; after MFMA q, the work items
+  // [q W / NM, (q + 1) W / NM) of the next slice (W = 2 NS items, NM MFMAs).
+  constexpr int NM = RB * CB, W = 2 * NS;
+  auto slice_even_next = [&](const Ops &o, const Buf &u, int i, Ops &d, bool next) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      mfma(o, q);
+#pragma unroll
+      for (int w = q * W / NM; w < (q + 1) * W / NM; ++w) even_item(u, i, d, next, w >> 1, w & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto slice_odd_next = [&](const Ops &o, const Buf &u, int i, Ops &d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      mfma(o, q);
+#pragma unroll
+      for (int w = q * W / NM; w < (q + 1) * W / NM; ++w) odd_item(u, i, d, w >> 1, w & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // A clean step whose slice-0 operands are already in op0: slices 1.. of
+  // u, and slice 0 of the following step un (unused after the last step:
+  // its registers then hold a re-read step).
+  auto run_step = [&](const Buf &u, const Buf &un) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kHW; ++i) {
+      slice_odd_next(op0, u, i, op1);
+      if (i + 1 < kHW)
+        slice_even_next(op1, u, i + 1, op0, false);
+      else
+        slice_even_next(op1, un, 0, op0, true);
+    }
+  };
+  // One slice on its own, pad elements masked in A (the steps after the
+  // pipelined loop).
+  auto unpack_masked = [&](const Buf &u, int j, Ops &o, int s) __attribute__((always_inline)) {
+    const int64_t e = (int64_t)(s * kSW + kHW * h + (j >> 1)) * 64 + 32 * (j & 1);
+    const uint32_t v = valid_bits(e, K);
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      const v4i c = fp4_chunk(u[p][j], c8, c2);
+      o.s[p] = p < RB ? mask4(c, v) : c;
+    }
+  };
+
+  // Two step register sets in ping-pong: the loads of step s+1 are issued
+  // at the start of step s (a scheduling barrier keeps them there), and its
+  // first slice is unpacked during step s's last one.  The loop runs whole
+  // pairs of clean steps; the load past the last pair re-reads its second
+  // step (in bounds, unused).  What is left -- an odd clean step and the
+  // partial last step (K not a multiple of 64 * SW) -- runs after the loop
+  // one slice at a time with the pad elements masked in A (a clean step's
+  // mask keeps every element).
+  Buf u0, u1;
+  const int npair = nclean >> 1;
+  if (npair > 0) {
+    load_step(0, u0);
+#pragma unroll
+    for (int w = 0; w < W; ++w) even_item(u0, 0, op0, false, w >> 1, w & 1);
+    for (int s = 0; s < 2 * npair; s += 2) {
+      load_step(s + 1, u1);
+      __builtin_amdgcn_sched_barrier(0);
+      run_step(u0, u1);
+      load_step(s + 2 < 2 * npair ? s + 2 : s + 1, u0);
+      __builtin_amdgcn_sched_barrier(0);
+      run_step(u1, u0);
+    }
+  }
+  for (int s = 2 * npair; s < nsteps; ++s) {
+    load_step(s, u0);  // words past K: garbage (masked) or 0 (past the rows)
+#pragma unroll
+    for (int j = 0; j < 2 * kHW; ++j) {
+      unpack_masked(u0, j, op0, s);
+#pragma unroll
+      for (int q = 0; q < NM; ++q) mfma(op0, q);
+    }
   }
 }
 
@@ -112,7 +363,7 @@ __global__ void __launch_bounds__(256, MINB)
   static_assert(!is_repack(EPI) || CB % 2 == 0, "repack pairs 32-column tiles");
   static_assert(SW == 4 || SW == 8, "two or four words per lane per step");
   constexpr int BM = WR * RB * 32, BN = WC * CB * 32;
-  constexpr int kSW = SW, kHW = SW / 2;  // words per step, per lane
+  constexpr int kHW = SW / 2;  // words per step and lane
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -153,24 +404,15 @@ __global__ void __launch_bounds__(256, MINB)
     boff[cb] = (uint32_t)(c * kw * 8 + h * (kHW * 8));
   }
 
-  // Per-column epilogue operands, fetched before the K loop: the scale, or
-  // the threshold as an fp32 bound that is exact against the (exact, |d| <=
-  // K <= 2^24) accumulators -- +inf / -inf outside [-K, K] -- and the flip
-  // word of each 64-column pair.
+  // Per-column epilogue operands, fetched before the K loop.
   float a_pre[CB];
   uint64_t f_pre[CB / 2 > 0 ? CB / 2 : 1];
+  {
+    int nc[CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int n = n0 + cb * 32 + li;
-    a_pre[cb] = (EPI == BNN_EPI_SCALED && n < N) ? ep.alpha[n] : 0.0f;
-    if (EPI == kEpiRepackThr) {
-      const int32_t t = thr_of(ep, n, N);
-      a_pre[cb] = t >= K ? __builtin_inff() : (t < -K ? -__builtin_inff() : (float)t);
-    }
+    for (int cb = 0; cb < CB; ++cb) nc[cb] = n0 + cb * 32;
+    epilogue_operands<EPI, CB>(ep, nc, li, N, K, a_pre, f_pre);
   }
-#pragma unroll
-  for (int cp = 0; cp < CB / 2; ++cp)
-    f_pre[cp] = EPI == kEpiRepackThr ? flip_of(ep, (n0 >> 6) + cp, N) : 0;
   v16f acc[RB][CB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -179,183 +421,24 @@ __global__ void __launch_bounds__(256, MINB)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  const int nsteps = (kw + kSW - 1) / kSW;
-  const int nclean = (K >> 6) / kSW;  // steps with every element inside K
-  const uint32_t c8 = 0x88888888u, c2 = 0x22222222u;
-
-  // Step registers: 32-bit chunks, [operand][chunk] with chunk 2i + q = half
-  // q of this lane's word i.
-  typedef uint32_t ABuf[RB][2 * kHW];
-  typedef uint32_t BBuf[CB][2 * kHW];
-  auto load_step = [&](int s, ABuf &a, BBuf &bb) __attribute__((always_inline)) {
-    const int so = s * (kSW * 8);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int j = 0; j < kHW / 2; ++j) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[rb] + 16 * j, so, 0);
-        a[rb][4 * j + 0] = v.x; a[rb][4 * j + 1] = v.y;
-        a[rb][4 * j + 2] = v.z; a[rb][4 * j + 3] = v.w;
-      }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int j = 0; j < kHW / 2; ++j) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(bres, boff[cb] + 16 * j, so, 0);
-        bb[cb][4 * j + 0] = v.x; bb[cb][4 * j + 1] = v.y;
-        bb[cb][4 * j + 2] = v.z; bb[cb][4 * j + 3] = v.w;
-      }
-  };
-  // Slices.  Slice j of a step (j = 2i + q: half q of this lane's word i)
-  // unpacks RB + CB operand sets and feeds RB * CB MFMAs.  The slices run as
-  // a software pipeline: while the MFMAs of slice j issue, the VALU unpacks
-  // slice j + 1 (of the next step after a step's last slice) into the other
-  // of two operand register sets, interleaved one MFMA to three or four
-  // VALU ops (the matrix unit and the VALU then work side by side in one
-  // wave instead of in turns).
-  struct Ops {
-    v4i a[RB], b[CB];
-  };
-  Ops op0, op1;
-  auto unpack = [&](const ABuf &a, const BBuf &bb, int j, Ops &o, bool masked, int s) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) o.a[rb] = fp4_chunk(a[rb][j], c8, c2);
-    if (masked) {
-      const int64_t e = (int64_t)(s * kSW + kHW * h + (j >> 1)) * 64 + 32 * (j & 1);
-      const uint32_t v = valid_bits(e, K);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o.a[rb] = mask4(o.a[rb], v);
-    }
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o.b[cb] = fp4_chunk(bb[cb][j], c8, c2);
-  };
-  auto mfmas = [&](const Ops &o) __attribute__((always_inline)) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            fp4_operand(o.a[rb]), fp4_operand(o.b[cb]), acc[rb][cb], kFmtFp4, kFmtFp4, 0,
-            kScaleOne, 0, kScaleOne);
-  };
-  // One MFMA, then 7 (RB + CB) / (RB CB) VALU ops on average, for every
-  // MFMA of a slice.
-  auto interleave = [&]() __attribute__((always_inline)) { interleave_groups<0, RB * CB, 7 * (RB + CB)>(); };
-  // A clean step whose slice-0 operands are already in set 0: slices 1.. of
-  // (a, bb), and slice 0 of the following step (an, bn).
-  auto run_step = [&](const ABuf &a, const BBuf &bb, const ABuf &an, const BBuf &bn) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < 2 * kHW; j += 2) {
-      unpack(a, bb, j + 1, op1, false, 0);
-      mfmas(op0);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-      // the next step's first slice (unused after the last step: its
-      // registers then hold a re-read step)
-      if (j + 2 < 2 * kHW)
-        unpack(a, bb, j + 2, op0, false, 0);
-      else
-        unpack(an, bn, 0, op0, false, 0);
-      mfmas(op1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // Two step register sets in ping-pong: the loads of step s+1 are issued
-  // at the start of step s (a scheduling barrier keeps them there), and its
-  // first slice is unpacked during step s's last one.  The loop runs whole
-  // pairs of clean steps; the load past the last pair re-reads its second
-  // step (in bounds, unused).  What is left -- an odd clean step and the
-  // partial last step (K not a multiple of 64 * SW) -- runs after the loop
-  // one slice at a time with the pad elements masked in A (a clean step's
-  // mask keeps every element).
-  ABuf a0, a1;
-  BBuf b0, b1;
-  const int npair = nclean >> 1;
-  if (npair > 0) {
-    load_step(0, a0, b0);
-    unpack(a0, b0, 0, op0, false, 0);
-    for (int s = 0; s < 2 * npair; s += 2) {
-      load_step(s + 1, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      run_step(a0, b0, a1, b1);
-      load_step(s + 2 < 2 * npair ? s + 2 : s + 1, a0, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      run_step(a1, b1, a0, b0);
-    }
-  }
-  for (int s = 2 * npair; s < nsteps; ++s) {
-    load_step(s, a0, b0);  // words past K: garbage (masked) or 0 (past the rows)
-#pragma unroll
-    for (int j = 0; j < 2 * kHW; ++j) {
-      unpack(a0, b0, j, op0, true, s);
-      mfmas(op0);
-    }
-  }
+  // in VGPRs, opaque to the compiler, so that every mask is one
+  // v_and_or_b32 (gfx9 VOP3 encodings take no literal)
+  const uint32_t c8 = settled(0x88888888u), c2 = settled(0x22222222u);
+  k_loop<RB, CB, SW>(acc, ares, bres, aoff, boff, K, kw, h, c8, c2);
+  // Every load has been waited for before the stores (the compiler would
+  // otherwise wait before each store).
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
 
   // Epilogue.  acc[rb][cb][v] is the exact integer dot of row
   // m0 + rb*32 + 8(v/4) + 4h + v%4 and column n0 + cb*32 + li.
-  // Every load is waited for once here (the scales were loaded before the K
-  // loop and the last prefetch re-read a step), so that no store below waits.
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
-  if (is_repack(EPI)) {
-    const int nw = (N + 63) >> 6;
+  int mr[RB], nc[CB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+  for (int rb = 0; rb < RB; ++rb) mr[rb] = m0 + rb * 32;
 #pragma unroll
-      for (int cp = 0; cp < CB / 2; ++cp) {
-        const int na = n0 + (2 * cp) * 32 + li, nb2 = na + 32;
-        const int wi = (n0 >> 6) + cp;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // bit set (-1) where the dot is <= the threshold (0 for the plain repack)
-          const uint64_t lo = __builtin_amdgcn_ballot_w64(na < N && acc[rb][2 * cp][v] <= a_pre[2 * cp]);
-          const uint64_t hi =
-              __builtin_amdgcn_ballot_w64(nb2 < N && acc[rb][2 * cp + 1][v] <= a_pre[2 * cp + 1]);
-          const int r0 = m0 + rb * 32 + 8 * (v >> 2) + (v & 3);
-          // lane 0 writes row r0, lane 32 writes row r0 + 4
-          const int r = r0 + 4 * h;
-          const uint64_t word = (h ? ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32))
-                                   : ((hi << 32) | (lo & 0xFFFFFFFFull))) ^ f_pre[cp];
-          if (li == 0 && r < M && wi < nw) static_cast<uint64_t *>(yv)[(int64_t)r * nw + wi] = word;
-        }
-      }
-  } else {
-    // Row r(v) = 8 (v / 4) + v % 4 of a 32-row tile (plus 4h).  Tiles wholly
-    // inside M store their 16 values without a row test (straight-line
-    // stores: no branch per value).
-    const int64_t ld = N;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int mt = m0 + rb * 32 + 4 * h;  // row of v = 0 for this lane
-      const bool full_rows = m0 + rb * 32 + 32 <= M;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int n = n0 + cb * 32 + li;
-        if (n >= N) continue;
-        const float a = a_pre[cb];
-        const int64_t base = (int64_t)mt * ld + n;
-        auto put = [&](int v) __attribute__((always_inline)) {
-          // (8 (v / 4) + v % 4) * ld is the same for every lane
-          const int64_t o = base + (int64_t)(8 * (v >> 2) + (v & 3)) * ld;
-          if (EPI == BNN_EPI_I32)
-            static_cast<int32_t *>(yv)[o] = (int)acc[rb][cb][v];
-          else
-            static_cast<float *>(yv)[o] = __fmul_rn(acc[rb][cb][v], a);
-        };
-        if (full_rows) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) put(v);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (mt + 8 * (v >> 2) + (v & 3) < M) put(v);
-        }
-      }
-    }
-  }
+  for (int cb = 0; cb < CB; ++cb) nc[cb] = n0 + cb * 32;
+  store_tiles<EPI, RB, CB>(acc, a_pre, f_pre, mr, nc, h, li, yv, M, N);
 }
+
 
 template <int EPI, int WR, int WC, int RB, int CB, int SW, int MINB>
 hipError_t launch_cfg(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y, int M,
@@ -380,7 +463,9 @@ hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const EpiParams &e
   // still give every CU at least one block and K is long enough for the K
   // loop (not the epilogue) to dominate a tile.
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  if (big >= 256 && K >= 2048) return launch_cfg<EPI, BNN_MFMA_BIG>(xp, wp, ep, y, M, N, K, s);
+  if (big >= 256 && K >= 2048) {
+    return launch_cfg<EPI, 2, 2, 4, 4, 4, 1>(xp, wp, ep, y, M, N, K, s);
+  }
   return launch_cfg<EPI, 4, 1, 2, 2, 8, 2>(xp, wp, ep, y, M, N, K, s);  // 256 x 64
 }
 

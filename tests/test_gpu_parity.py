@@ -188,6 +188,40 @@ def test_mfma_large_tiles_ragged(K):
     assert np.array_equal(yi[mi, ni], oracle.dot_pairs(xc, wc, K, mi, ni))
 
 
+@pytest.mark.parametrize("K", [2049, 4096, 4163, 6000, 32767])
+def test_mfma_large_products_n_multiple_of_8(K):
+    # 18 x 18 block tiles of 256 x 256 with N % 8 == 0 (the common case of
+    # the last test's shapes): K = 4096 whole steps, 2049 and 4163 a partial
+    # last step, 6000 an odd number of whole steps and a partial one, 32767
+    # a long K loop.
+    # Ragged block row and column compared in full against the oracle,
+    # sampled outputs elsewhere, and the whole product against the VALU
+    # kernel.
+    M, N = 17 * 256 + 37, 17 * 256 + 40
+    say("mfma large products", M, N, K)
+    rng = np.random.default_rng(K + 29)
+    xg, xc = rand_packed(rng, M, K)
+    wg, wc = rand_packed(rng, N, K)
+    alpha = (rng.standard_normal(N) * 3).astype(np.float32)
+    alpha[::7] = 0.0
+    xd, wd, ad = to_dev_words(xg), to_dev_words(wg), torch.from_numpy(alpha).to(DEV)
+    yi = bnn.gemm_ex(xd, wd, K, bnn.EPI_I32, bnn.ALGO_MFMA)
+    ys = bnn.gemm_ex(xd, wd, K, bnn.EPI_SCALED, bnn.ALGO_MFMA, alpha=ad)
+    assert torch.equal(yi, bnn.gemm_ex(xd, wd, K, bnn.EPI_I32, bnn.ALGO_TILED))
+    assert torch.equal(ys, bnn.gemm_ex(xd, wd, K, bnn.EPI_SCALED, bnn.ALGO_TILED, alpha=ad))
+    yi, ys = yi.cpu().numpy(), ys.cpu().numpy()
+    edge_r = np.arange(17 * 256, M)
+    edge_c = np.arange(17 * 256, N)
+    assert np.array_equal(yi[edge_r], oracle.gemm_i32(xc[edge_r], wc, K))
+    assert_scaled_equal(ys[edge_r], oracle.gemm_scaled(xc[edge_r], wc, alpha, K))
+    assert np.array_equal(yi[:, edge_c], oracle.gemm_i32(xc, wc[edge_c], K))
+    assert_scaled_equal(ys[:, edge_c], oracle.gemm_scaled(xc, wc[edge_c], alpha[edge_c], K))
+    mi, ni = _sample_pairs(rng, M, N, 20000)
+    d = oracle.dot_pairs(xc, wc, K, mi, ni)
+    assert np.array_equal(yi[mi, ni], d)
+    assert np.array_equal(ys[mi, ni], (d.astype(np.float32) * alpha[ni]).astype(np.float32))
+
+
 def test_named_entry_points_match_oracle():
     rng = np.random.default_rng(5)
     for M, N, K in [(1, 777, 1000), (200, 300, 700)]:
