@@ -46,6 +46,10 @@ constexpr int kMaxW = 8;        // words of K per layer (K <= 512)
 #ifndef BNN_CHAIN_MIN_BLOCKS
 #define BNN_CHAIN_MIN_BLOCKS 2
 #endif
+// Weight words each thread loads in one go before the first input batch
+// (12 x 256 covers 512 -> 256 -> 128 -> 64; larger weights load the rest
+// after it).
+constexpr int kWeightLoads = 12;
 // Layer-1 column tiles accumulated while the input streams in (their
 // accumulators stay live across the K steps; 4 keeps two waves per SIMD).
 constexpr int kPipeTiles = BNN_CHAIN_PIPE;
@@ -54,30 +58,44 @@ constexpr int kPipeTiles = BNN_CHAIN_PIPE;
 // into the 64-bit words of the wave's 32 rows: out[r * nw + wi].
 // acc[v]: row 8 (v / 4) + 4 h + v % 4, column li (+ 32 for the second tile);
 // the low ballot bits are row r's 32 columns, the high bits those of row r + 4.
-// The two ballots are wave-uniform, so both rows' words are put together
-// in scalar registers and lane 0 writes them (no per-lane select).  A bit is
-// set where the exact dot is <= the column's bound (tb: the layer's
-// per-column thresholds as exact fp32 bounds, 0 without thresholds), then
-// the group's flip word is applied.
+// Each ballot half is written into lane r (or r + 4) of a register pair, so
+// that lane r ends up holding row r's word and one store of lanes 0-31
+// writes all 32 words.  A bit is set where the exact dot is <= the column's
+// bound (tb: the layer's per-column thresholds as exact fp32 bounds, 0
+// without thresholds), then the group's flip word is applied.
+// v with lane L set to s (wave-uniform).
+template <int L>
+__device__ __forceinline__ int write_lane(int v, uint32_t s) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "n"(L));
+  return v;
+}
+
+// Ballots of accumulator register V of both tiles into lanes r and r + 4 of
+// lo / hi (r = 8 (V / 4) + V % 4), then the next register.
+template <int V>
+__device__ __forceinline__ void repack_rows(const v16f &t0, const v16f &t1, float b0, float b1,
+                                            int &lo, int &hi) {
+  if constexpr (V < 16) {
+    constexpr int r = 8 * (V >> 2) + (V & 3);
+    const uint64_t m0 = __builtin_amdgcn_ballot_w64(t0[V] <= b0);
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(t1[V] <= b1);
+    lo = write_lane<r>(lo, (uint32_t)m0);
+    hi = write_lane<r>(hi, (uint32_t)m1);
+    lo = write_lane<r + 4>(lo, (uint32_t)(m0 >> 32));
+    hi = write_lane<r + 4>(hi, (uint32_t)(m1 >> 32));
+    repack_rows<V + 1>(t0, t1, b0, b1, lo, hi);
+  }
+}
+
 template <bool THR>
 __device__ __forceinline__ void repack_pair(const v16f &t0, const v16f &t1, uint64_t *out, int nw,
                                             int wi, int lane, const float *tb, const uint64_t *fw) {
-  uint64_t *col = out + wi;
   const int li = lane & 31;
   const float b0 = THR ? tb[64 * wi + li] : 0.0f, b1 = THR ? tb[64 * wi + 32 + li] : 0.0f;
+  int lo = 0, hi = 0;  // lane r < 32: row r's word, columns 0-31 / 32-63
+  repack_rows<0>(t0, t1, b0, b1, lo, hi);
   const uint64_t f = THR ? fw[wi] : 0;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const uint64_t lo = __builtin_amdgcn_ballot_w64(t0[v] <= b0);
-    const uint64_t hi = __builtin_amdgcn_ballot_w64(t1[v] <= b1);
-    const int r = 8 * (v >> 2) + (v & 3);
-    const uint64_t w_r = ((hi << 32) | (lo & 0xFFFFFFFFull)) ^ f;           // lanes 0-31: row r
-    const uint64_t w_r4 = ((hi & 0xFFFFFFFF00000000ull) | (lo >> 32)) ^ f;  // lanes 32-63: row r + 4
-    if (lane == 0) {
-      col[r * nw] = w_r;
-      col[(r + 4) * nw] = w_r4;
-    }
-  }
+  if (lane < kRows) out[lane * nw + wi] = (((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo) ^ f;
 }
 
 // Columns n_begin .. N-1 of one layer for the wave's 32 rows.  a: the wave's
@@ -218,27 +236,41 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
     }
   };
 
+  // The weights of all three layers into LDS (block-wide).  Their loads go
+  // out first, all at once (at most kWeightLoads words per thread): the
+  // first input batch, issued right behind them, then queues after the
+  // weights rather than the weights after the whole grid's first batches.
   Raw8 raw[8];
-  load_batch(0, raw);
-  // The weights of all three layers into LDS (block-wide), behind the first
-  // input loads.
   {
     const int total = nw1 + nw2 + nw3;
-    for (int i0 = 0; i0 < total; i0 += 4 * 256) {
-      uint64_t v[4];
+    // word i of the three matrices back to back (a word past them re-reads
+    // the last one and is not stored): one unconditional load each, so
+    // that all of them are in flight together
+    auto word_at = [&](int i) __attribute__((always_inline)) {
+      const int j = i < total ? i : total - 1;
+      const uint64_t *p = j < nw1 ? w1 + j : (j < nw1 + nw2 ? w2 + (j - nw1) : w3 + (j - nw1 - nw2));
+      return *p;
+    };
+    uint64_t v[kWeightLoads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 256 + tid;
-        v[u] = i < nw1 ? w1[i] : i < nw1 + nw2 ? w2[i - nw1] : i < total ? w3[i - nw1 - nw2] : 0;
-      }
+    for (int u = 0; u < kWeightLoads; ++u) v[u] = word_at(u * 256 + tid);
+    // the last layer's scales (N3 <= 512), likewise ahead of the input
+    float al[2] = {0.0f, 0.0f};
+    if (alpha) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * 256 + tid;
-        if (i < total) lds[i] = v[u];
-      }
+      for (int u = 0; u < 2; ++u) al[u] = alpha[u * 256 + tid < N3 ? u * 256 + tid : N3 - 1];
     }
-    // the last layer's scales
-    for (int i = tid; alpha && i < N3; i += 256) AL[i] = alpha[i];
+    load_batch(0, raw);
+#pragma unroll
+    for (int u = 0; u < kWeightLoads; ++u) {
+      const int i = u * 256 + tid;
+      if (i < total) lds[i] = v[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (alpha && u * 256 + tid < N3) AL[u * 256 + tid] = al[u];
+    // larger weights: the rest word by word
+    for (int i = kWeightLoads * 256 + tid; i < total; i += 256) lds[i] = word_at(i);
     // repack bounds and flip words of the hidden layers
     for (int i = tid; THR && i < N1 + N2; i += 256)
       TB1[i] = i < N1 ? repack_bound(rp.thr1, i, K0) : repack_bound(rp.thr2, i - N1, N1);
@@ -264,7 +296,10 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   for (int b = 0; b < hw0; ++b) {
     pack_batch(b, raw);
     if (b + 1 < hw0) load_batch(b + 1, raw);
-    __syncthreads();  // batch b's words are in LDS
+    // batch b's words are in LDS: written and read back by this wave only
+    // (its own rows), and a wave's LDS accesses take effect in program
+    // order, so the wave waits for no other
+    __builtin_amdgcn_wave_barrier();
     v8i a0, a1;
     fp4_operands(h0[li * kw0 + h * hw0 + b], c8, c2, a0, a1);
 #pragma unroll
@@ -285,9 +320,9 @@ __global__ void __launch_bounds__(256, BNN_CHAIN_MIN_BLOCKS)
   if (nt1 > kPipeTiles)  // wider first layers: the remaining columns from the packed rows
     chain_layer<true, THR>(h0, kw0, W1, N1, 32 * kPipeTiles, h1, TB1, FW1, nullptr, nullptr,
                            row0, M, lane);
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();  // h1: this wave's rows only
   chain_layer<true, THR>(h1, kw1, W2, N2, 0, h2, TB2, FW2, nullptr, nullptr, row0, M, lane);
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();  // h2: this wave's rows only
   chain_layer<false, false>(h2, kw2, W3, N3, 0, nullptr, nullptr, nullptr, alpha ? AL : nullptr,
                             y, row0, M, lane);
 }
