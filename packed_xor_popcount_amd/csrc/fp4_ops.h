@@ -31,6 +31,19 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
   return r;
 }
 
+// w << S as one v_lshlrev_b64 (the compiler splits a 64-bit shift whose
+// halves are used apart into two 32-bit ops).  `pinned`: volatile, so that
+// the scheduler keeps it where it is written.
+template <int S>
+__device__ __forceinline__ uint64_t shl64(uint64_t w, bool pinned = false) {
+  uint64_t r;
+  if (pinned)
+    asm volatile("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(w));
+  else
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(w));
+  return r;
+}
+
 // Operands of both 32-element halves of a packed word w: register r of the
 // half's operand is ((half << (3 - r)) & 0x88888888) | 0x22222222.  One
 // 64-bit shift serves both halves: the bits it carries from the low half
@@ -38,7 +51,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 // Eleven VALU ops for 64 elements.
 __device__ __forceinline__ void fp4_operands(uint64_t w, uint32_t c8, uint32_t c2, v8i &lo,
                                              v8i &hi) {
-  const uint64_t s1 = w << 1, s2 = w << 2, s3 = w << 3;
+  const uint64_t s1 = shl64<1>(w), s2 = shl64<2>(w), s3 = shl64<3>(w);
   lo[0] = (int)and_or((uint32_t)s3, c8, c2);
   lo[1] = (int)and_or((uint32_t)s2, c8, c2);
   lo[2] = (int)and_or((uint32_t)s1, c8, c2);

@@ -75,19 +75,6 @@ __device__ __forceinline__ v4i fp4_chunk(uint32_t c, uint32_t c8, uint32_t c2) {
   return o;
 }
 
-// w << s as one v_lshlrev_b64 (the compiler splits a 64-bit shift whose
-// halves are used apart into two 32-bit ops).  `pinned`: volatile, so that
-// the scheduler keeps it where it is written.
-template <int S>
-__device__ __forceinline__ uint64_t shl64(uint64_t w, bool pinned) {
-  uint64_t r;
-  if (pinned)
-    asm volatile("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(w));
-  else
-    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "i"(S), "v"(w));
-  return r;
-}
-
 // The eight-register operand of the FP4 MFMA: an FP4 operand uses the first
 // four registers only.
 __device__ __forceinline__ v8i fp4_operand(v4i o) {
