@@ -34,6 +34,7 @@
 //    8th of the rows run on one XCD (its L2 then reads those rows once).
 #include "../../include/bnn.h"
 #include "bnn_internal.h"
+#include "fp4_ops.h"
 
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
@@ -53,6 +54,33 @@ __device__ __forceinline__ uint32_t sign_pair(uint32_t c_shifted, uint32_t mask,
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(c_shifted), "v"(mask), "v"(ones));
   return r;
+}
+
+// w << s as one 64-bit shift for a shift count that is a constant after
+// unrolling (the switch folds away).  Both 32-bit halves of w come out
+// shifted for the pair registers: the bits the shift carries from the low
+// half into the high half land below bit s <= 15, under the sign positions
+// 15 and 31 that sign_pair keeps.
+__device__ __forceinline__ uint64_t shl64_const(uint64_t w, int s) {
+  switch (s) {
+    case 0: return w;
+    case 1: return shl64<1>(w);
+    case 2: return shl64<2>(w);
+    case 3: return shl64<3>(w);
+    case 4: return shl64<4>(w);
+    case 5: return shl64<5>(w);
+    case 6: return shl64<6>(w);
+    case 7: return shl64<7>(w);
+    case 8: return shl64<8>(w);
+    case 9: return shl64<9>(w);
+    case 10: return shl64<10>(w);
+    case 11: return shl64<11>(w);
+    case 12: return shl64<12>(w);
+    case 13: return shl64<13>(w);
+    case 14: return shl64<14>(w);
+    case 15: return shl64<15>(w);
+    default: return w << s;
+  }
 }
 
 __device__ __forceinline__ float dot2(uint32_t xpair, uint32_t wpair, float acc) {
@@ -166,17 +194,22 @@ __global__ void __launch_bounds__(256)
         }
       }
 #pragma unroll
-      for (int v = 0; v < VEC; ++v)
+      for (int v = 0; v < VEC; ++v) {
+        // pair registers of both chunks of word v (16 per chunk and column):
+        // one 64-bit shift serves chunk 0 (low half) and chunk 1 (high half)
+        uint32_t b2[2][P][16];
+#pragma unroll
+        for (int p = 0; p < P; ++p)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const uint64_t sh = shl64_const(w[p][v], 15 - j);
+            b2[0][p][j] = sign_pair((uint32_t)sh, mask, ones);
+            b2[1][p][j] = sign_pair((uint32_t)(sh >> 32), mask, ones);
+          }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          // chunk qi = 2v + h of this unit: 16 pair registers per column
-          uint32_t b[P][16];
-#pragma unroll
-          for (int p = 0; p < P; ++p) {
-            const uint32_t c = (uint32_t)(w[p][v] >> (32 * h));
-#pragma unroll
-            for (int j = 0; j < 16; ++j) b[p][j] = sign_pair(c << (15 - j), mask, ones);
-          }
+          // chunk qi = 2v + h of this unit
+          const uint32_t(&b)[P][16] = b2[h];
 #pragma unroll
           for (int rr = 0; rr < kGemvRows; ++rr) {
             if (rr >= M) break;
@@ -197,6 +230,7 @@ __global__ void __launch_bounds__(256)
             }
           }
         }
+      }
     }
 
 #pragma unroll
