@@ -441,6 +441,21 @@ hipError_t launch_cfg(const uint64_t *xp, const uint64_t *wp, const EpiParams &e
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails, which only affects the choice of tile shape).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int EPI>
 hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const EpiParams &ep, void *y, int M,
                       int N, int K, hipStream_t s) {
@@ -448,9 +463,21 @@ hipError_t launch_epi(const uint64_t *xp, const uint64_t *wp, const EpiParams &e
   if (N <= 64) return launch_cfg<EPI, 4, 1, 1, 2, 8, 2>(xp, wp, ep, y, M, N, K, s);  // 128 x 64
   // Large products: 256 x 256 block tiles of 4 x 4 wave tiles, while they
   // still give every CU at least one block and K is long enough for the K
-  // loop (not the epilogue) to dominate a tile.
+  // loop (not the epilogue) to dominate a tile.  One block runs per CU, so
+  // the tiles run in rounds of one per CU; when 320 x 192 block tiles (5 x 3
+  // wave tiles: 15 instead of 16 MFMA tiles a wave, 2.93 instead of 2.75
+  // unpack VALU per MFMA) need no more rounds, their shorter rounds win
+  // (4096 x 11008: 754 tiles in 3 rounds against 688 in 3).  Repacked
+  // outputs pair 32-column tiles and keep 4 x 4.
   const int64_t big = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
   if (big >= 256 && K >= 2048) {
+    if constexpr (!is_repack(EPI)) {
+      const int64_t cus = cu_count();
+      const int64_t t53 = (int64_t)((M + 319) / 320) * ((N + 191) / 192);
+      const int64_t r44 = (big + cus - 1) / cus, r53 = (t53 + cus - 1) / cus;
+      if (r53 * 31 < r44 * 32)  // rounds x tile work (15.5 against 16, the VALU counted in)
+        return launch_cfg<EPI, 2, 2, 5, 3, 4, 1>(xp, wp, ep, y, M, N, K, s);
+    }
     return launch_cfg<EPI, 2, 2, 4, 4, 4, 1>(xp, wp, ep, y, M, N, K, s);
   }
   return launch_cfg<EPI, 4, 1, 2, 2, 8, 2>(xp, wp, ep, y, M, N, K, s);  // 256 x 64

@@ -150,9 +150,11 @@ def test_gemm_all_epilogues(M, N, K, algo):
 
 @pytest.mark.parametrize("K", [1000, 2049, 2304, 4163])
 def test_mfma_large_tiles_ragged(K):
-    # Large products with K >= 2048 run 256 x 256 block tiles of 4 x 4 wave
-    # tiles on the matrix cores (K = 2049: a partial last step; 2304: an odd
-    # number of whole steps; 4163: both), shorter K the 256 x 64 tiles:
+    # Large products with K >= 2048 run 320 x 192 block tiles of 5 x 3 wave
+    # tiles (word outputs; 286 tiles in two rounds here) or 256 x 256 of
+    # 4 x 4 (repacked outputs) on the matrix cores (K = 2049: a partial last
+    # step; 2304: an odd number of whole steps; 4163: both), shorter K the
+    # 256 x 64 tiles:
     # ragged M, N and K past every tile edge, garbage pad bits; the ragged
     # block row and block column are compared in full, the rest on sampled
     # outputs, for every epilogue.
@@ -188,16 +190,18 @@ def test_mfma_large_tiles_ragged(K):
     assert np.array_equal(yi[mi, ni], oracle.dot_pairs(xc, wc, K, mi, ni))
 
 
-@pytest.mark.parametrize("K", [2049, 4096, 4163, 6000, 32767])
-def test_mfma_large_products_n_multiple_of_8(K):
-    # 18 x 18 block tiles of 256 x 256 with N % 8 == 0 (the common case of
-    # the last test's shapes): K = 4096 whole steps, 2049 and 4163 a partial
-    # last step, 6000 an odd number of whole steps and a partial one, 32767
-    # a long K loop.
-    # Ragged block row and column compared in full against the oracle,
-    # sampled outputs elsewhere, and the whole product against the VALU
-    # kernel.
-    M, N = 17 * 256 + 37, 17 * 256 + 40
+@pytest.mark.parametrize("M,N,K", [(4389, 4392, 2049), (4389, 4392, 4096), (4389, 4392, 4163),
+                                   (4389, 4392, 6000), (4389, 4392, 32767),
+                                   (4000, 4072, 2049), (4000, 4072, 4163)])
+def test_mfma_large_products_n_multiple_of_8(M, N, K):
+    # Large products with N % 8 == 0: K = 4096 whole steps, 2049 and 4163 a
+    # partial last step, 6000 an odd number of whole steps and a partial one,
+    # 32767 a long K loop.  4389 x 4392 runs the word outputs on 320 x 192
+    # block tiles (5 x 3 wave tiles: 322 tiles in two rounds against 324 of
+    # 256 x 256), 4000 x 4072 on 256 x 256 (256 tiles, one round); the
+    # repacked outputs always on 256 x 256.  Ragged block row and column
+    # compared in full against the oracle, sampled outputs elsewhere, and
+    # the whole product against the VALU kernel.
     say("mfma large products", M, N, K)
     rng = np.random.default_rng(K + 29)
     xg, xc = rand_packed(rng, M, K)
@@ -210,8 +214,10 @@ def test_mfma_large_products_n_multiple_of_8(K):
     assert torch.equal(yi, bnn.gemm_ex(xd, wd, K, bnn.EPI_I32, bnn.ALGO_TILED))
     assert torch.equal(ys, bnn.gemm_ex(xd, wd, K, bnn.EPI_SCALED, bnn.ALGO_TILED, alpha=ad))
     yi, ys = yi.cpu().numpy(), ys.cpu().numpy()
-    edge_r = np.arange(17 * 256, M)
-    edge_c = np.arange(17 * 256, N)
+    # the last 320-row and 192-column block tiles (they contain the last
+    # 256-row and 256-column ones' ragged edges too)
+    edge_r = np.arange(min((M - 1) // 320 * 320, (M - 1) // 256 * 256), M)
+    edge_c = np.arange(min((N - 1) // 192 * 192, (N - 1) // 256 * 256), N)
     assert np.array_equal(yi[edge_r], oracle.gemm_i32(xc[edge_r], wc, K))
     assert_scaled_equal(ys[edge_r], oracle.gemm_scaled(xc[edge_r], wc, alpha, K))
     assert np.array_equal(yi[:, edge_c], oracle.gemm_i32(xc, wc[edge_c], K))
