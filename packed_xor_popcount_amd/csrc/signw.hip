@@ -445,32 +445,35 @@ __global__ void __launch_bounds__(256, MINB)
   const int wrow = (wave / WC) * (RB * 32);  // this wave's first row inside the block tile
   auto compute = [&](const unsigned char *buf, const uint64_t (&wcur)[CB]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      // weight chunk q of each column, pre-shifted by 4 for lane half 0
-      uint32_t cq[CB];
+    for (int t = 0; t < 2; ++t) {
+      // activation fragments of both chunks q (one LDS read each)
+      bf16x8 afr[2][RB];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          afr[q][rb] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4 *>(
+                          buf + (wrow + rb * 32 + li) * kARowBytes + q * 64 + t * 32 + h * 16));
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t c = (uint32_t)(wcur[cb] >> (32 * q));
-        cq[cb] = h ? c : (c << 4);
-      }
+        // the column's word, pre-shifted by 4 for lane half 0; one 64-bit
+        // shift per pair position gives both chunks' pair registers (what it
+        // carries into the high half lands below the sign positions)
+        const uint64_t w = h ? wcur[cb] : (wcur[cb] << 4);
+        uint32_t r[2][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 bfr[CB];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          uint32_t r4[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) r4[j] = sign_pair(cq[cb] << (11 - 8 * t - j), mask, ones);
-          bfr[cb] = __builtin_bit_cast(bf16x8, make_uint4(r4[0], r4[1], r4[2], r4[3]));
+        for (int j = 0; j < 4; ++j) {
+          const uint64_t sh = shl64_const(w, 11 - 8 * t - j);
+          r[0][j] = sign_pair((uint32_t)sh, mask, ones);
+          r[1][j] = sign_pair((uint32_t)(sh >> 32), mask, ones);
         }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const uint4 av = *reinterpret_cast<const uint4 *>(
-              buf + (wrow + rb * 32 + li) * kARowBytes + q * 64 + t * 32 + h * 16);
-          const bf16x8 afr = __builtin_bit_cast(bf16x8, av);
+        for (int q = 0; q < 2; ++q) {
+          const bf16x8 bfr = __builtin_bit_cast(bf16x8, make_uint4(r[q][0], r[q][1], r[q][2], r[q][3]));
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[cb], acc[rb][cb], 0, 0, 0);
+          for (int rb = 0; rb < RB; ++rb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[q][rb], bfr, acc[rb][cb], 0, 0, 0);
         }
       }
     }
