@@ -334,6 +334,13 @@ __global__ void __launch_bounds__(256, MINB)
   // Two LDS tiles: step s is staged into tile s % 2 while the other one may
   // still be read by step s - 1, so one barrier per step suffices.
   __shared__ __attribute__((aligned(16))) unsigned char as[2][BM * kARowBytes];
+  // The weight words of the block's BN columns for the same step, staged
+  // beside the activations (thread t loads column t's word two steps ahead,
+  // like its activation pieces, and every lane reads its columns' words back):
+  // loaded straight into each lane per step instead, the words' latency was
+  // exposed at every step.
+  static_assert(BN <= 256, "one weight word per thread and step");
+  __shared__ __attribute__((aligned(16))) uint64_t ws[2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -353,16 +360,23 @@ __global__ void __launch_bounds__(256, MINB)
   const int m0 = tm * BM + (wave / WC) * (RB * 32);
   const int n0 = tn * BN + (wave % WC) * (CB * 32);
 
-  // Weight rows of this lane's columns (clamped; columns past N are never stored).
-  const uint64_t *bcol[CB];
+  // Scales of this lane's columns (clamped; columns past N are never stored),
+  // and the weight row this thread stages (column tid of the block tile).
   float a_pre[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     int n = n0 + cb * 32 + li;
     n = n < N ? n : N - 1;
-    bcol[cb] = wp + (int64_t)n * kw;
     a_pre[cb] = SCALED ? alpha[n] : 1.0f;
   }
+  const uint64_t *wrow_t;
+  {
+    int n = tn * BN + (tid < BN ? tid : BN - 1);
+    n = n < N ? n : N - 1;
+    wrow_t = wp + (int64_t)n * kw;
+  }
+  // this wave's first column inside the block tile
+  const int wcol = (wave % WC) * (CB * 32);
 
   // Fragments staged by this thread: f = tid + 256 i is (row f / 8, chunk
   // (f / 4) & 1, t = (f / 2) & 1, h = f & 1) and holds the four pairs
@@ -443,7 +457,10 @@ __global__ void __launch_bounds__(256, MINB)
 
   const uint32_t mask = kSignMask, ones = kPlusOnes;
   const int wrow = (wave / WC) * (RB * 32);  // this wave's first row inside the block tile
-  auto compute = [&](const unsigned char *buf, const uint64_t (&wcur)[CB]) {
+  auto compute = [&](const unsigned char *buf, const uint64_t *wbuf) {
+    uint64_t wcur[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) wcur[cb] = wbuf[wcol + cb * 32 + li];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // activation fragments of both chunks q (one LDS read each)
@@ -480,57 +497,62 @@ __global__ void __launch_bounds__(256, MINB)
   };
 
   // Two register stages in flight over the full steps: while step s is
-  // staged and computed, the activation loads of step s + 2 are in flight.
-  // The loop is unrolled by two so that each stage keeps its own registers,
-  // and no loaded value is ever copied (a copy waits for its load): a stage's
-  // activation registers are reloaded right after they are written to LDS,
-  // its weight words right after the step that used them.  Loads past the
-  // last full step re-read it (in bounds, unused).
+  // staged and computed, the activation and weight loads of step s + 2 are
+  // in flight.  The loop is unrolled by two so that each stage keeps its own
+  // registers, and no loaded value is ever copied (a copy waits for its
+  // load): a stage's registers are reloaded right after they are written to
+  // LDS, the weight word first (the oldest load of a stage is waited for
+  // first).  Loads past the last full step re-read it (in bounds, unused).
   const int nfull = K / kBK;
   const int last = nfull - 1;
   Stage ra, rb;
-  uint64_t wa[CB], wb[CB];
+  uint64_t wra = 0, wrb = 0;  // this thread's staged weight word of each stage
   if (nfull > 0) {
+    wra = wrow_t[0];
     load_full(0, ra);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][0];
     const int s1 = last < 1 ? last : 1;
+    wrb = wrow_t[s1];
     load_full(s1, rb);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wb[cb] = bcol[cb][s1];
   }
-  for (int s = 0; s < nfull; s += 2) {
+  // Whole pairs of steps in the loop (no branch inside it, so that the wait
+  // counts the compiler derives at the loop head are exact, not the merge of
+  // two paths); an odd last full step, already loaded into stage a, after.
+  for (int s = 0; s + 1 < nfull; s += 2) {
     const int s2 = s + 2 < last ? s + 2 : last;
+    const int s3 = s + 3 < last ? s + 3 : last;
     store_a(ra, as[0]);
+    if (BN == 256 || tid < BN) ws[0][tid] = wra;
     __syncthreads();
+    wra = wrow_t[s2];
     load_full(s2, ra);
 #if BNN_SIGNW_PIN
     __builtin_amdgcn_sched_barrier(0);
 #endif
-    compute(as[0], wa);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][s2];
-    if (s + 1 < nfull) {
-      const int s3 = s + 3 < last ? s + 3 : last;
-      store_a(rb, as[1]);
-      __syncthreads();
-      load_full(s3, rb);
+    compute(as[0], ws[0]);
+    store_a(rb, as[1]);
+    if (BN == 256 || tid < BN) ws[1][tid] = wrb;
+    __syncthreads();
+    wrb = wrow_t[s3];
+    load_full(s3, rb);
 #if BNN_SIGNW_PIN
-      __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_sched_barrier(0);
 #endif
-      compute(as[1], wb);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) wb[cb] = bcol[cb][s3];
-    }
+    compute(as[1], ws[1]);
+  }
+  if (nfull & 1) {  // uniform branch; stage a holds step nfull - 1
+    store_a(ra, as[0]);
+    if (BN == 256 || tid < BN) ws[0][tid] = wra;
+    __syncthreads();
+    compute(as[0], ws[0]);
   }
   if (nfull < kw) {  // the partial last step, zero past K (uniform branch)
     load_tail(nfull, ra);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) wa[cb] = bcol[cb][nfull];
+    wra = wrow_t[nfull];
     __syncthreads();  // both tiles are free
     store_a(ra, as[0]);
+    if (BN == 256 || tid < BN) ws[0][tid] = wra;
     __syncthreads();
-    compute(as[0], wa);
+    compute(as[0], ws[0]);
   }
 
   // Nothing is left in flight, so that no store below waits; tiles wholly
