@@ -508,11 +508,18 @@ __global__ void __launch_bounds__(256, MINB)
   Stage ra, rb;
   uint64_t wra = 0, wrb = 0;  // this thread's staged weight word of each stage
   if (nfull > 0) {
+    // the issue order pinned (weight word, then activations, stage a then
+    // stage b), the same as in the loop, so that the loop head's waits are
+    // exact: each waits for its own stage and leaves the other one in flight
     wra = wrow_t[0];
+    __builtin_amdgcn_sched_barrier(0);
     load_full(0, ra);
+    __builtin_amdgcn_sched_barrier(0);
     const int s1 = last < 1 ? last : 1;
     wrb = wrow_t[s1];
+    __builtin_amdgcn_sched_barrier(0);
     load_full(s1, rb);
+    __builtin_amdgcn_sched_barrier(0);
   }
   // Whole pairs of steps in the loop (no branch inside it, so that the wait
   // counts the compiler derives at the loop head are exact, not the merge of
@@ -524,6 +531,7 @@ __global__ void __launch_bounds__(256, MINB)
     if (BN == 256 || tid < BN) ws[0][tid] = wra;
     __syncthreads();
     wra = wrow_t[s2];
+    __builtin_amdgcn_sched_barrier(0);
     load_full(s2, ra);
 #if BNN_SIGNW_PIN
     __builtin_amdgcn_sched_barrier(0);
@@ -533,6 +541,7 @@ __global__ void __launch_bounds__(256, MINB)
     if (BN == 256 || tid < BN) ws[1][tid] = wrb;
     __syncthreads();
     wrb = wrow_t[s3];
+    __builtin_amdgcn_sched_barrier(0);
     load_full(s3, rb);
 #if BNN_SIGNW_PIN
     __builtin_amdgcn_sched_barrier(0);
