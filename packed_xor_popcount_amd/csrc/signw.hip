@@ -254,46 +254,79 @@ __global__ void __launch_bounds__(256)
     }
   };
 
-  // The first step's W words and scales go out before the activation rows
-  // are staged, so the staging overlaps their latency; later steps run in
-  // pairs whose operands are loaded one step ahead (single-step blocks load
-  // nothing extra; the register sets are never copied).
-  StepRegs ra;
-  load_step(blockIdx.x, ra);
   // Stage the activation rows once per block in pair order: word p of chunk
   // q holds (x[32q + p], x[32q + p + 16]).  Item i builds words 4j .. 4j+3
   // of one chunk (one 16-byte LDS store) from the 8-byte pieces
   // x[32q + 4j .. +3] and x[32q + 16 + 4j .. +3]; pieces that reach past K
   // (or rows that are not 8-byte aligned) are read element by element.
-  {
-    const int chunks = units * VEC * 2;
-    const int total = M * chunks * 4;
-    for (int i = tid; i < total; i += 256) {
+  // A thread loads kStageItems items before it waits on any.  The loads of
+  // the first items go out before the first step's W words and scales:
+  // loads retire in order, so the staging then waits only for itself while
+  // the W words stay in flight across the barrier.
+  constexpr int kStageItems = 4;
+  const int chunks = units * VEC * 2;
+  const int total = M * chunks * 4;
+  typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x), (short)0, 0x7FFFFFFF, 0x00020000);
+  uint32_t pc[kStageItems][4];
+  bool fast[kStageItems];
+  auto stage_load = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < kStageItems; ++e) {
+      const int i = i0 + 256 * e;
       const int j = i & 3;
       const int rq = i >> 2;
       const int m = rq / chunks, q = rq - m * chunks;
       const int64_t k = (int64_t)q * 32 + 4 * j;
-      uint32_t lo0, lo1, hi0, hi1;
-      if (XV8 && k + 20 <= K) {
-        const uint2 a = *reinterpret_cast<const uint2 *>(x + m * ldx + k);
-        const uint2 b = *reinterpret_cast<const uint2 *>(x + m * ldx + k + 16);
-        lo0 = a.x; lo1 = a.y; hi0 = b.x; hi1 = b.y;
-      } else {
-        lo0 = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 1, K) << 16);
-        lo1 = x_at(x, ldx, m, k + 2, K) | (x_at(x, ldx, m, k + 3, K) << 16);
-        hi0 = x_at(x, ldx, m, k + 16, K) | (x_at(x, ldx, m, k + 17, K) << 16);
-        hi1 = x_at(x, ldx, m, k + 18, K) | (x_at(x, ldx, m, k + 19, K) << 16);
+      fast[e] = XV8 & (i < total) & (k + 20 <= K);
+      if (XV8) {
+        // Out-of-range byte offsets (element-wise or absent items) read 0.
+        const uint32_t off = fast[e] ? (uint32_t)((m * ldx + k) * 2) : 0x80000000u;
+        const v2u lo = __builtin_amdgcn_raw_buffer_load_b64(xres, off, 0, 0);
+        const v2u hi = __builtin_amdgcn_raw_buffer_load_b64(xres, off + 32, 0, 0);
+        pc[e][0] = lo.x; pc[e][1] = lo.y; pc[e][2] = hi.x; pc[e][3] = hi.y;
       }
-      uint4 v;
-      v.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
-      v.y = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
-      v.z = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
-      v.w = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
-      const int u = q / (VEC * 2), qi = q - u * (VEC * 2);
-      *reinterpret_cast<uint4 *>(xs + ((size_t)m * units + u) * kUnitBytes + qi * 64 + j * 16) = v;
     }
-    __syncthreads();
+  };
+  auto stage_store = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < kStageItems; ++e) {
+      const int i = i0 + 256 * e;
+      if (i < total) {
+        const int j = i & 3;
+        const int rq = i >> 2;
+        const int m = rq / chunks, q = rq - m * chunks;
+        const int64_t k = (int64_t)q * 32 + 4 * j;
+        if (!fast[e]) {
+          pc[e][0] = x_at(x, ldx, m, k, K) | (x_at(x, ldx, m, k + 1, K) << 16);
+          pc[e][1] = x_at(x, ldx, m, k + 2, K) | (x_at(x, ldx, m, k + 3, K) << 16);
+          pc[e][2] = x_at(x, ldx, m, k + 16, K) | (x_at(x, ldx, m, k + 17, K) << 16);
+          pc[e][3] = x_at(x, ldx, m, k + 18, K) | (x_at(x, ldx, m, k + 19, K) << 16);
+        }
+        uint4 v;
+        v.x = __builtin_amdgcn_perm(pc[e][2], pc[e][0], 0x05040100u);
+        v.y = __builtin_amdgcn_perm(pc[e][2], pc[e][0], 0x07060302u);
+        v.z = __builtin_amdgcn_perm(pc[e][3], pc[e][1], 0x05040100u);
+        v.w = __builtin_amdgcn_perm(pc[e][3], pc[e][1], 0x07060302u);
+        const int u = q / (VEC * 2), qi = q - u * (VEC * 2);
+        *reinterpret_cast<uint4 *>(xs + ((size_t)m * units + u) * kUnitBytes + qi * 64 + j * 16) =
+            v;
+      }
+    }
+  };
+  stage_load(tid);
+  // The first step's operands; later steps run in pairs whose operands are
+  // loaded one step ahead (single-step blocks load nothing extra; the
+  // register sets are never copied).
+  StepRegs ra;
+  load_step(blockIdx.x, ra);
+  stage_store(tid);
+  for (int i0 = tid + 256 * kStageItems; i0 < total; i0 += 256 * kStageItems) {
+    stage_load(i0);
+    stage_store(i0);
   }
+  __syncthreads();
   for (int step = blockIdx.x; step < nsteps; step += 2 * gridDim.x) {
     const int sb = step + gridDim.x, sa = step + 2 * gridDim.x;
     StepRegs rb;
@@ -596,8 +629,10 @@ __global__ void __launch_bounds__(256, MINB)
 template <int L, int VEC, int P, bool SCALED>
 hipError_t launch_gemv_lp(const uint16_t *x, int64_t ldx, const uint64_t *wp, const float *alpha,
                           float *y, int M, int N, int K, int kw, hipStream_t s) {
-  // 8-byte activation pieces need 8-byte aligned row starts.
-  const bool xv8 = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0 || M == 1);
+  // 8-byte activation pieces need 8-byte aligned row starts, and the buffer
+  // loads 32-bit byte offsets (all of X below 2 GiB).
+  const bool xv8 = ((uintptr_t)x % 8 == 0) && (ldx % 4 == 0 || M == 1) &&
+                   ((int64_t)(M - 1) * ldx + K) * 2 < (int64_t(1) << 31);
   constexpr int CB = 4 * (64 / L) * P;
   const int64_t steps = ((int64_t)N + CB - 1) / CB;
   const int64_t cap = 256 * 8;
