@@ -147,6 +147,30 @@ def test_signw_strided_and_unaligned_rows():
         assert_exact(bnn.gemm_signw_bf16(x4, wd, K, None, algo).cpu().numpy(), s4, None)
 
 
+@pytest.mark.parametrize("M,K", [(1, 4096), (1, 20), (3, 1000), (8, 2049), (2, 96), (5, 4163)])
+@pytest.mark.parametrize("off,pad", [(0, 0), (4, 0), (0, 4), (8, 8), (1, 0), (0, 9)])
+def test_signw_gemv_staging_alignments(M, K, off, pad):
+    """The batch GEMV stages the activation rows from 8-byte pieces (row
+    starts 8-byte aligned) or element by element (else, and for pieces that
+    reach past K): row starts at every alignment (offsets of 0, 1, 4 and 8
+    elements, row strides K + 0/4/8/9), ragged last chunks and K below one
+    chunk, against the oracle bit for bit."""
+    rng = np.random.default_rng(M * 1000 + K + 17 * off + pad)
+    N = 300
+    ld = K + pad
+    flat = int_bf16(rng, 1, off + M * ld + 16).ravel()
+    dflat = bf16_dev(flat)
+    view = dflat[off:off + M * ld].view(M, ld)[:, :K]
+    xb = np.ascontiguousarray(flat[off:off + M * ld].reshape(M, ld)[:, :K])
+    wp = rand_packed(rng, N, K)
+    alpha = (rng.standard_normal(N) * 2).astype(np.float32)
+    s = oracle.dot_signw_bf16(xb, wp, K)
+    say("signw gemv staging", M, K, "offset", off, "pad", pad, "ptr % 16", view.data_ptr() % 16)
+    got = bnn.gemm_signw_bf16(view, to_dev_words(wp), K, torch.from_numpy(alpha).to(DEV),
+                              bnn.ALGO_GEMV)
+    assert_exact(got.cpu().numpy(), s, alpha)
+
+
 def test_signw_gemv_rejects_oversized_rows():
     x = torch.zeros(2, 70001, dtype=torch.bfloat16, device=DEV)
     w = torch.zeros(3, oracle.words(70001), dtype=torch.int64, device=DEV)
