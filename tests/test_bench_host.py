@@ -74,7 +74,7 @@ def test_ring_plan_keeps_timed_weights_cold(R, steps, warmup):
 
 
 def test_headline_ring_exceeds_the_infinity_cache():
-    # the driver's --steps 20 --warmup 5: each timed 2 MiB weight copy was
+    # a short run (--steps 20 --warmup 5): each timed 2 MiB weight copy was
     # last read before 383 other copies (766 MiB > 2 x 256 MB) were read
     plan = bench.ring_plan(bench.GEMV_RING, 20, 5)
     gap_bytes = bench.cold_gap_entries(plan) * 4096 * 64 * 8
@@ -90,6 +90,6 @@ def test_cold_gap_detects_a_warm_replay():
     assert bench.cold_gap_entries(plan) == 19
 
 
-def test_bench_parses_driver_flags():
+def test_bench_parses_step_flags():
     a = bench.parse(["--gpus", "1", "--steps", "20", "--warmup", "5"])
     assert (a.gpus, a.steps, a.warmup, a.workload) == (1, 20, 5, "gemv_4096")
