@@ -414,8 +414,8 @@ def gemv_leg(steps, warmup, calib=None, rows=None, eager=False):
     gbs = nbytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS,
-            "traffic": recorded_traffic("gemv_4096_traffic.md", GEMV_SOURCES)
-            if not rows else None,
+            "traffic": recorded_traffic("gemv_4096_traffic.md" if not rows
+                                        else "gemv_stream_traffic.md", GEMV_SOURCES),
             "kernel": "gemv_act_kernel (bf16 activations packed in-kernel, alpha-scaled)",
             "kernel_avg_us": ms * 1e3, "algorithmic_bytes_per_launch": nbytes,
             "note": "a step is one launch: the kernel's average duration is the step time of "
@@ -468,7 +468,8 @@ def named_gemv_leg(steps, warmup, calib=None):
     nbytes = N * kw * 8 + kw * 8 + N * 4 + N * 4   # Wp + xp + alpha + y
     gbs = nbytes / (ms1 * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": gbs / HBM_PEAK_GBS,
+            "traffic": recorded_traffic("named_gemv_4096_traffic.md", GEMV_SOURCES),
             "kernel": "gemv_act_kernel (packed activations, alpha-scaled), via "
                       "bnn_gemm_u64_scaled",
             "kernel_avg_us": ms1 * 1e3, "algorithmic_bytes_per_launch": nbytes}
