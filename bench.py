@@ -353,6 +353,15 @@ def calibrate():
     out["mfma_fp4"] = {"rate": rate / 1e12, "unit": "TFLOP/s (FP4)",
                        "frac_of_nominal": rate / MFMA_FP4_PEAK_OPS, "sclk_mhz": mhz,
                        "probe": f"{mb} blocks x 4 waves x {mi} x 4 MFMA 32x32x64 FP4"}
+
+    def mp():
+        run.last = cal.mfma_fp4_pm1(mb, mi)
+    ms, mhz = run(mp)
+    rate = flops / (ms * 1e-3)
+    out["mfma_fp4_pm1"] = {"rate": rate / 1e12, "unit": "TFLOP/s (FP4)",
+                           "frac_of_nominal": rate / MFMA_FP4_PEAK_OPS, "sclk_mhz": mhz,
+                           "probe": f"{mb} blocks x 4 waves x {mi} x 4 MFMA 32x32x64 FP4 on "
+                                    "pseudo-random +-1 operands, another pair each MFMA"}
     buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
     best = None
     for rb in (1024, 2048, 4096, 8192):   # the best launch shape is the calibrated rate
@@ -611,6 +620,11 @@ def ffn_leg(n, calib=None):
             "launches_timed": n, "algorithmic_ops_per_launch": ops,
             "frac_of_valu_popcount_peak": ach / ALU_PEAK_BINARY_OPS}
     roof = with_calibration(roof, calib, "mfma_fp4")
+    if calib and "mfma_fp4_pm1" in calib:
+        # the matrix cores' rate on +-1 operands that change every MFMA (the
+        # data this product feeds them)
+        roof["calibrated_pm1_peak"] = calib["mfma_fp4_pm1"]["rate"]
+        roof["calibrated_pm1_frac"] = roof["achieved"] / calib["mfma_fp4_pm1"]["rate"]
     valu_rate = ops / (ms_valu * 1e-3)
     abl = {"valu_xor_popcount_us": ms_valu * 1e3, "mfma_fp4_us": ms_mfma2 * 1e3,
            "valu_xor_popcount_frac_of_valu_peak": valu_rate / ALU_PEAK_BINARY_OPS,

@@ -9,7 +9,8 @@
  *     ("Binary Math Effectiveness -- why / how / when", section 2.1
  *     "Arithmetic": one XOR + popcount per 64-bit word);
  *   - the rate of the FP4 matrix-core instruction the large-M product runs
- *     on (v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands);
+ *     on (v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands), with fixed
+ *     operands and with +-1 operands that change from one MFMA to the next;
  *   - the read rate of HBM with the 16-byte non-temporal loads the
  *     weight-streaming kernels use (same page, sections 2.2-2.3: a batch-1
  *     product is bound by the bytes it streams);
@@ -51,6 +52,12 @@ int bnn_calib_valu(int64_t *out, int64_t blocks, int64_t iters, void *stream);
  * runs `iters` iterations of 4 independent FP4 32x32x64 MFMAs with unit
  * scales, i.e. 4 * iters * 131072 flops per wave. */
 int bnn_calib_mfma_fp4(int64_t *out, int64_t blocks, int64_t iters, void *stream);
+
+/* The same matrix-core probe on the data the packed product feeds: four
+ * operand pairs of pseudo-random +-1 FP4 nibbles, and each of the 4 MFMAs
+ * of an iteration takes another pair than the one before it (the rate of
+ * the instruction depends on the operand bits it switches). */
+int bnn_calib_mfma_fp4_pm1(int64_t *out, int64_t blocks, int64_t iters, void *stream);
 
 /* HBM probe: `blocks` blocks of 256 threads read `bytes` bytes (a positive
  * multiple of 16) of `src` (16-byte aligned) once, 16 bytes per load with

@@ -16,7 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libbnn_calib.so")
 
-EXPORTED = ("bnn_calib_valu", "bnn_calib_mfma_fp4", "bnn_calib_read", "bnn_calib_wallclock_hz")
+EXPORTED = ("bnn_calib_valu", "bnn_calib_mfma_fp4", "bnn_calib_mfma_fp4_pm1", "bnn_calib_read",
+            "bnn_calib_wallclock_hz")
 
 _lib = None
 
@@ -31,8 +32,9 @@ def library():
     P, I64 = ctypes.c_void_p, ctypes.c_int64
     lib.bnn_calib_valu.argtypes = [P, I64, I64, P]
     lib.bnn_calib_mfma_fp4.argtypes = [P, I64, I64, P]
+    lib.bnn_calib_mfma_fp4_pm1.argtypes = [P, I64, I64, P]
     lib.bnn_calib_read.argtypes = [P, I64, P, I64, P]
-    for n in ("bnn_calib_valu", "bnn_calib_mfma_fp4", "bnn_calib_read"):
+    for n in ("bnn_calib_valu", "bnn_calib_mfma_fp4", "bnn_calib_mfma_fp4_pm1", "bnn_calib_read"):
         getattr(lib, n).restype = ctypes.c_int
     lib.bnn_calib_wallclock_hz.argtypes, lib.bnn_calib_wallclock_hz.restype = [], I64
     _lib = lib
@@ -66,6 +68,15 @@ def mfma_fp4(blocks: int, iters: int, device="cuda:0") -> torch.Tensor:
     st = library().bnn_calib_mfma_fp4(ctypes.c_void_p(out.data_ptr()), blocks, iters,
                                       _stream(device))
     return _done(st, out, blocks, "bnn_calib_mfma_fp4")
+
+
+def mfma_fp4_pm1(blocks: int, iters: int, device="cuda:0") -> torch.Tensor:
+    """As mfma_fp4, with pseudo-random +-1 operands that change from one MFMA
+    to the next."""
+    out = _records(blocks, device)
+    st = library().bnn_calib_mfma_fp4_pm1(ctypes.c_void_p(out.data_ptr()), blocks, iters,
+                                          _stream(device))
+    return _done(st, out, blocks, "bnn_calib_mfma_fp4_pm1")
 
 
 def read(buf: torch.Tensor, blocks: int) -> torch.Tensor:

@@ -60,16 +60,35 @@ __global__ void __launch_bounds__(256) calib_valu_kernel(int64_t *out, int64_t i
   if (s == 0x12345678u) out[4 * (int64_t)gridDim.x] = s;  // keeps the loop live
 }
 
+// A 32-bit mix of x (an integer hash; only its bits matter here).
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7FEB352Du;
+  x ^= x >> 15;
+  x *= 0x846CA68Bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// PM1 false: the four MFMAs of an iteration share one operand pair whose
+// FP4 +1.0 (0x2) / -1.0 (0xA) nibbles vary by lane only.  PM1 true: four
+// operand pairs of pseudo-random +-1 nibbles, and MFMA c of an iteration
+// takes A set c and B set c + 1 (mod 4), so that every MFMA sees another
+// +-1 pattern than the one before it, as in the packed product.
+template <bool PM1>
 __global__ void __launch_bounds__(256) calib_mfma_kernel(int64_t *out, int64_t iters) {
   int64_t *rec = out + 4 * (int64_t)blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  v8i a, b;
+  const uint32_t lane = threadIdx.x & 63;
+  v8i a[4], b[4];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    // FP4 +1.0 (0x2) / -1.0 (0xA) nibbles, varying by lane
-    a[r] = r < 4 ? (int)(0x22222222u | (((uint32_t)lane * 0x01010101u) & 0x88888888u)) : 0;
-    b[r] = r < 4 ? (int)(0x22222222u | (((uint32_t)lane * 0x10101010u) & 0x88888888u)) : 0;
-  }
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t ha = PM1 ? mix32(lane * 97u + c * 13u + r * 7u + 1u) : lane * 0x01010101u;
+      const uint32_t hb = PM1 ? mix32(lane * 89u + c * 31u + r * 5u + 1000u) : lane * 0x10101010u;
+      a[c][r] = r < 4 ? (int)(0x22222222u | (ha & 0x88888888u)) : 0;
+      b[c][r] = r < 4 ? (int)(0x22222222u | (hb & 0x88888888u)) : 0;
+    }
   v16f acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -80,8 +99,8 @@ __global__ void __launch_bounds__(256) calib_mfma_kernel(int64_t *out, int64_t i
   for (int64_t i = 0; i < iters; ++i) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], 4, 4, 0, 0x7F7F7F7F,
-                                                              0, 0x7F7F7F7F);
+      acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a[PM1 ? c : 0], b[PM1 ? (c + 1) & 3 : 0], acc[c], 4, 4, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
   }
   stamp(rec, false);
   float s = 0.0f;
@@ -138,7 +157,15 @@ int bnn_calib_valu(int64_t *out, int64_t blocks, int64_t iters, void *stream) {
 int bnn_calib_mfma_fp4(int64_t *out, int64_t blocks, int64_t iters, void *stream) {
   const int st = check(out, blocks, iters);
   if (st != BNN_OK) return st;
-  hipLaunchKernelGGL(calib_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0,
+  hipLaunchKernelGGL(calib_mfma_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), out, iters);
+  return hipGetLastError() == hipSuccess ? BNN_OK : BNN_E_LAUNCH;
+}
+
+int bnn_calib_mfma_fp4_pm1(int64_t *out, int64_t blocks, int64_t iters, void *stream) {
+  const int st = check(out, blocks, iters);
+  if (st != BNN_OK) return st;
+  hipLaunchKernelGGL(calib_mfma_kernel<true>, dim3((unsigned)blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), out, iters);
   return hipGetLastError() == hipSuccess ? BNN_OK : BNN_E_LAUNCH;
 }

@@ -65,6 +65,8 @@ def test_calibration_library_exports_its_header():
     # host-side validation, no launch
     assert lib.bnn_calib_valu(None, 1, 1, None) == E_NULL
     assert lib.bnn_calib_mfma_fp4(FAKE, 0, 1, None) == E_SHAPE
+    assert lib.bnn_calib_mfma_fp4_pm1(FAKE, 1, 0, None) == E_SHAPE
+    assert lib.bnn_calib_mfma_fp4_pm1(None, 1, 1, None) == E_NULL
     assert lib.bnn_calib_read(FAKE, 15, FAKE, 1, None) == E_SHAPE
     assert lib.bnn_calib_read(FAKE_ODD, 16, FAKE, 1, None) == E_ALIGN
     deps = subprocess.run(["readelf", "-d", bnn.library_path], capture_output=True, text=True,
