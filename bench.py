@@ -36,10 +36,12 @@ the path (each with its own roofline and CPU-oracle baseline):
   small          gemv_small and edge_1000 (latency-bound), with single-thread
                  oracle times.
   calibration    the rates this GPU sustains on register-only probes (VALU
-                 xor + popcount pairs, FP4 MFMA) and a streaming HBM read,
-                 with the shader clock measured during each probe; every
-                 roofline carries its fraction of the matching calibrated
-                 rate next to its fraction of the published peak.
+                 xor + popcount pairs, FP4 MFMA on fixed and on changing +-1
+                 operands) and a streaming HBM read, with the shader clock
+                 measured during each probe, and the cost of one launch of
+                 the batch-1 grid with no work in it; every roofline
+                 carries its fraction of the matching calibrated rate next
+                 to its fraction of the published peak.
 
 "roofline" reports the dominant kernel of a step: algorithmic bytes (or
 binary ops) per launch divided by its average launch duration, measured
@@ -362,6 +364,21 @@ def calibrate():
                            "frac_of_nominal": rate / MFMA_FP4_PEAK_OPS, "sclk_mhz": mhz,
                            "probe": f"{mb} blocks x 4 waves x {mi} x 4 MFMA 32x32x64 FP4 on "
                                     "pseudo-random +-1 operands, another pair each MFMA"}
+    # Launch floor: back-to-back graph replays of a kernel that does almost
+    # nothing (the VALU probe with one iteration) on the batch-1 GEMV's grid
+    # of 512 blocks x 256 threads.
+    import ctypes
+    lib = cal.library()
+    rec = torch.zeros(4 * 512 + 1, dtype=torch.int64, device=dev)
+
+    def noop():
+        st = lib.bnn_calib_valu(ctypes.c_void_p(rec.data_ptr()), 512, 1,
+                                ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"bnn_calib_valu: status {st}")
+    out["launch_floor"] = {"us": graph_ms(noop, 1024) * 1e3,
+                           "probe": "HIP graph of 1024 launches of 512 blocks x 256 threads, "
+                                    "64 register-only lane-ops per thread"}
     buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
     best = None
     for rb in (1024, 2048, 4096, 8192):   # the best launch shape is the calibrated rate
@@ -429,6 +446,9 @@ def gemv_leg(steps, warmup, calib=None, rows=None, eager=False):
             "kernel_avg_us": ms * 1e3, "algorithmic_bytes_per_launch": nbytes,
             "note": "a step is one launch: the kernel's average duration is the step time of "
                     "back-to-back graph replays (an upper bound: it includes launch gaps)"}
+    if calib and "launch_floor" in calib and not rows:
+        # what a launch of this grid costs with no work in it (same replay method)
+        roof["launch_floor_us"] = calib["launch_floor"]["us"]
     return dict(
         value=gbs, unit="GB/s", ms_per_step=ms, binary_gops=2.0 * N * K / (ms * 1e-3) / 1e9,
         config={"workload": "gemv_4096" if not rows else f"gemv_4096_stream_rows{N}", "M": 1,
@@ -951,7 +971,9 @@ def main():
         calib = calibrate()
         log("[bench] calibration: " + ", ".join(
             f"{k} {v['rate']:.1f} {v['unit']} (sclk {v['sclk_mhz'] or 0:.0f} MHz)"
-            for k, v in calib.items() if isinstance(v, dict)))
+            for k, v in calib.items() if isinstance(v, dict) and "rate" in v)
+            + (f", launch floor {calib['launch_floor']['us']:.2f} us" if "launch_floor" in calib
+               else ""))
         if wl == "calibrate":
             print(json.dumps({"metric": METRIC, "calibration": calib}), flush=True)
             return
