@@ -417,8 +417,8 @@ def calibrate():
     out["hbm"] = {"rate": buf.numel() / (ms * 1e-3) / 1e9, "unit": "GB/s",
                   "frac_of_nominal": buf.numel() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "sclk_mhz": mhz,
-                  "probe": f"1 GiB read once, 16-byte nt loads, 8 in flight per thread; best of "
-                           f"1024-8192 blocks ({rb})"}
+                  "probe": f"1 GiB read once, 16-byte nt loads, a contiguous 32 KiB per block "
+                           f"step; best of 1024-8192 blocks ({rb})"}
     del buf
     return out
 

@@ -61,8 +61,9 @@ int bnn_calib_mfma_fp4_pm1(int64_t *out, int64_t blocks, int64_t iters, void *st
 
 /* HBM probe: `blocks` blocks of 256 threads read `bytes` bytes (a positive
  * multiple of 16) of `src` (16-byte aligned) once, 16 bytes per load with
- * non-temporal loads, grid-stride: the practical read rate of this GPU's
- * HBM when the buffer is larger than the caches. */
+ * non-temporal loads; each block step reads a contiguous 32 KiB chunk and the
+ * blocks stride over the chunks: the practical read rate of this GPU's HBM
+ * when the buffer is larger than the caches. */
 int bnn_calib_read(const void *src, int64_t bytes, int64_t *out, int64_t blocks, void *stream);
 
 /* Frequency of the wall clock counter in Hz (0 if the runtime cannot tell). */

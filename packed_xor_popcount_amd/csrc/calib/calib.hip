@@ -111,23 +111,28 @@ __global__ void __launch_bounds__(256) calib_mfma_kernel(int64_t *out, int64_t i
   if (s == 1.2345f) out[4 * (int64_t)gridDim.x] = (int64_t)s;  // keeps the loop live
 }
 
-// Streaming read of `units` 16-byte units, grid-stride, several loads in
-// flight per thread; the folded value keeps every load live.
+// Streaming read of `units` 16-byte units: each block step reads a
+// contiguous chunk of 256 x 8 units (32 KiB, eight loads in flight per
+// thread), and the blocks stride over the chunks; the folded value keeps
+// every load live.  (Eight loads per thread spread a grid stride apart read
+// about 15 % slower: more DRAM pages open at once.)
 __global__ void __launch_bounds__(256)
     calib_read_kernel(const u32x4 *__restrict__ src, int64_t units, int64_t *out) {
   int64_t *rec = out + 4 * (int64_t)blockIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  constexpr int kU = 8;
+  constexpr int64_t kChunk = 256 * kU;
   uint32_t f = 0;
   stamp(rec, true);
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 7 * stride < units; i += 8 * stride) {
-    u32x4 v[8];
+  int64_t base = (int64_t)blockIdx.x * kChunk;
+  for (; base + kChunk <= units; base += (int64_t)gridDim.x * kChunk) {
+    u32x4 v[kU];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(src + i + j * stride);
+    for (int j = 0; j < kU; ++j) v[j] = __builtin_nontemporal_load(src + base + j * 256 + threadIdx.x);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    for (int j = 0; j < kU; ++j) f ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
   }
-  for (; i < units; i += stride) {
+  // the last partial chunk (units not a multiple of the chunk)
+  for (int64_t i = base + threadIdx.x; base < units && i < units; i += 256) {
     const u32x4 v = __builtin_nontemporal_load(src + i);
     f ^= v.x ^ v.y ^ v.z ^ v.w;
   }
