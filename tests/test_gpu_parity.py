@@ -593,3 +593,29 @@ def test_gemv_many_columns(M, N, K):
     assert np.array_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_I32).cpu().numpy(), ref)
     assert_scaled_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_SCALED, alpha=ad).cpu().numpy(), refs)
     assert np.array_equal(words_np(bnn.gemv_act(xd, wd, K, bnn.EPI_REPACK)), refp)
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [(1, 150001, 4096, torch.bfloat16),
+                                         (3, 150001, 4096, torch.float32),
+                                         (2, 600007, 200, torch.bfloat16),
+                                         (8, 600007, 200, torch.float32)])
+def test_gemv_multi_step_blocks(M, N, K, dtype):
+    # N beyond one step per persistent block: blocks of two or three steps
+    # (the streaming form: each step's operands loaded one step ahead, pairs
+    # of steps, an odd last step), real-valued and packed rows
+    say("gemv multi-step", M, N, K, dtype)
+    c = workloads.random_case(seed=N + K + M, M=M, N=N, K=K, dist="normal", dtype=dtype)
+    rng = np.random.default_rng(N + M)
+    wg, wc = rand_packed(rng, N, K)
+    rx = oracle.pack(host_input(c["x"]))
+    alpha = c["alpha"]
+    xd, wd, ad = c["x"].to(DEV), to_dev_words(wg), alpha.to(DEV)
+    xpd = to_dev_words(rx)
+    ref = oracle.gemm_i32(rx, wc, K)
+    refs = oracle.gemm_scaled(rx, wc, alpha.numpy(), K)
+    refp = oracle.sign_repack(rx, wc, K)
+    assert np.array_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_I32).cpu().numpy(), ref)
+    assert_scaled_equal(bnn.gemv_act(xd, wd, K, bnn.EPI_SCALED, alpha=ad).cpu().numpy(), refs)
+    assert np.array_equal(words_np(bnn.gemv_act(xd, wd, K, bnn.EPI_REPACK)), refp)
+    assert np.array_equal(bnn.gemm_u64(xpd, wd, K).cpu().numpy(), ref)
+    assert_scaled_equal(bnn.gemm_u64_scaled(xpd, wd, ad, K).cpu().numpy(), refs)
