@@ -181,9 +181,10 @@ def test_signw_gemv_rejects_oversized_rows():
 
 
 @pytest.mark.parametrize("M,K,N", [(256, 1024, 1024), (512, 2048, 2048), (16384, 1024, 1024)])
-def test_signw_page_shapes_sampled_rows(M, K, N):
+def test_signw_page_shapes_every_output(M, K, N):
     # the packed-sign kernel shapes of the "Triton Kernel Benchmark" section,
-    # N(0,1) activations and weights; every output of sampled rows
+    # N(0,1) activations and weights; every output against the oracle's
+    # float64 sums (16384 x 1024 x 1024: a few seconds of host time)
     g = torch.Generator().manual_seed(M + K)
     x = torch.randn(M, K, generator=g).to(torch.bfloat16)
     w = torch.randn(N, K, generator=g)
@@ -193,8 +194,6 @@ def test_signw_page_shapes_sampled_rows(M, K, N):
     alpha = w.abs().mean(dim=1).numpy().astype(np.float32)
     y = bnn.gemm_signw_bf16(x.to(DEV), wd, K, torch.from_numpy(alpha).to(DEV)).cpu().numpy()
     xb = x.view(torch.int16).numpy().view(np.uint16)
-    rng = np.random.default_rng(M)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 254)]))
-    s = oracle.dot_signw_bf16(np.ascontiguousarray(xb[rows]), wp, K)
-    absx = np.abs(bf16_values(xb[rows])).sum(axis=1)
-    assert_within_bound(y[rows], s, alpha, absx, K)
+    s = oracle.dot_signw_bf16(np.ascontiguousarray(xb), wp, K)
+    absx = np.abs(bf16_values(xb)).sum(axis=1)
+    assert_within_bound(y, s, alpha, absx, K)
