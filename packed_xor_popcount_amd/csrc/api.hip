@@ -39,7 +39,9 @@ bnn_status run_gemm(const uint64_t *xp, const uint64_t *wp, const bnn::EpiParams
                     int64_t M, int64_t N, int64_t K, int epilogue, int algo, hipStream_t s) {
   if (M == 0 || N == 0) return BNN_OK;
   if (algo == BNN_ALGO_AUTO) {
-    if (M <= kGemvMaxM)
+    if (K == 0)
+      algo = BNN_ALGO_TILED;  // no K loop: the smallest kernel writes the constant result
+    else if (M <= kGemvMaxM)
       algo = BNN_ALGO_GEMV;  // weight-streaming: HBM-bound
     else if (K <= bnn::kMfmaMaxK)
       algo = BNN_ALGO_MFMA;  // matrix cores: ~8x the VALU popcount rate

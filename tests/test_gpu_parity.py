@@ -242,12 +242,13 @@ def test_named_entry_points_match_oracle():
                               oracle.sign_repack(xc, wc, K))
 
 
-def test_k_zero_and_empty_products():
+@pytest.mark.parametrize("M", [1, 64])
+def test_k_zero_and_empty_products(M):
     for algo in ALGOS:
-        xd = torch.empty(64, 0, dtype=torch.int64, device=DEV)
+        xd = torch.empty(M, 0, dtype=torch.int64, device=DEV)
         wd = torch.empty(1000, 0, dtype=torch.int64, device=DEV)
         y = bnn.gemm_ex(xd, wd, 0, bnn.EPI_I32, algo)
-        assert y.shape == (64, 1000) and not y.any()
+        assert y.shape == (M, 1000) and not y.any()
         a = torch.randn(1000, device=DEV)
         assert not bnn.gemm_ex(xd, wd, 0, bnn.EPI_SCALED, algo, alpha=a).any()
         p = words_np(bnn.gemm_ex(xd, wd, 0, bnn.EPI_REPACK, algo))
